@@ -1,0 +1,162 @@
+"""fp64 CPU oracle for alternating attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the CPU-baseline leg of the
+benchmark may import this package.  It shares no code with the HIP library
+(``alternating_attention_amd``) and never imports it.
+
+Two independent implementations of the same definitions live here:
+
+* ``vga_oracle.c`` (plain C, fp64, OpenMP over (row, head)), loaded with
+  ctypes -- explicit column lists and a max-shifted softmax per row;
+* ``brute.py`` (numpy, fp64) -- the whole logit matrix with a mask and an
+  augmented mean column, for tiny inputs.
+
+What is computed follows the pages:
+
+* "VGGT CVPR25 Best Paper" notes, section "Alternating-Attention": frame-wise
+  self-attention, then global self-attention over every token of every frame.
+* "AVGGT: Rethinking Global Attention for Accelerating VGGT", technical summary,
+  section 3 (Methodology): early global layers become frame attention; the
+  rest run Subsampled Global Attention (all queries kept; K/V on a strided
+  patch grid; the diagonal kept; dropped columns replaced by one global mean;
+  one shared softmax over the three parts).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "vga_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libvga_oracle.so")
+
+MODE_FRAME, MODE_GLOBAL, MODE_SGA = 0, 1, 2
+_F32, _BF16 = 0, 1
+
+
+def build(force: bool = True) -> str:
+    """Compile vga_oracle.c with gcc into libvga_oracle.so (in-tree)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
+               _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build(force=False)
+    lib = ctypes.CDLL(_LIB_PATH)
+    i32, i64, dbl, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+    lib.vgao_select.restype = i64
+    lib.vgao_select.argtypes = [i32] * 8 + [vp, vp]
+    lib.vgao_dropped_mean.restype = i64
+    lib.vgao_dropped_mean.argtypes = [i32] * 7 + [vp, vp] + [i32] * 4 + [vp, vp]
+    lib.vgao_attention.restype = ctypes.c_int
+    lib.vgao_attention.argtypes = ([i32] * 8 + [dbl, vp, vp, vp] + [i32] * 6
+                                   + [vp, i64, vp, i32])
+    lib.vgao_schedule.restype = ctypes.c_int
+    lib.vgao_schedule.argtypes = [i32, i32, i32, vp]
+    lib.vgao_max_threads.restype = i32
+    lib.vgao_max_threads.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _elements(x: np.ndarray):
+    """(contiguous array, dtype code): float32 as is, bf16 as raw uint16 bits."""
+    if x.dtype == np.float32:
+        return np.ascontiguousarray(x), _F32
+    if x.dtype in (np.uint16, np.int16):
+        return np.ascontiguousarray(x).view(np.uint16), _BF16
+    raise TypeError("oracle inputs are float32 or bf16 bits (uint16), got %s" % x.dtype)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def select(N, L, gh, gw, sh, sw, oh, ow):
+    """SGA key selection: (keep_idx int64[N*kpf], keep_mask uint8[N*L])."""
+    lib = _load()
+    T = N * L
+    idx = np.empty(T, dtype=np.int64)
+    mask = np.empty(T, dtype=np.uint8)
+    n = lib.vgao_select(N, L, gh, gw, sh, sw, oh, ow, _ptr(idx), _ptr(mask))
+    return idx[:n].copy(), mask
+
+
+def dropped_mean(k, v, N, L, gh, gw, sh, sw, oh, ow):
+    """(kmean [H,d] fp64, vmean [H,d] fp64, |D|) over the SGA-dropped tokens."""
+    lib = _load()
+    kk, dt = _elements(k)
+    vv, dt2 = _elements(v)
+    assert dt == dt2 and kk.shape == vv.shape and kk.ndim == 3
+    _, H, d = kk.shape
+    km = np.zeros((H, d))
+    vm = np.zeros((H, d))
+    nd = lib.vgao_dropped_mean(N, L, gh, gw, H, d, dt, _ptr(kk), _ptr(vv),
+                               sh, sw, oh, ow, _ptr(km), _ptr(vm))
+    return km, vm, int(nd)
+
+
+def attention(mode, q, k, v, N, L, gh, gw, scale, sga=None, rows=None, threads=0):
+    """fp64 attention output [len(rows) or T, H, d] for mode FRAME/GLOBAL/SGA.
+
+    q, k, v: [T, H, d] float32, or bf16 given as uint16 bits.
+    sga: dict(stride_h, stride_w, phase_h, phase_w, diagonal, mean_fill)."""
+    lib = _load()
+    qq, dt = _elements(q)
+    kk, dtk = _elements(k)
+    vv, dtv = _elements(v)
+    assert dt == dtk == dtv and qq.shape == kk.shape == vv.shape and qq.ndim == 3
+    T, H, d = qq.shape
+    assert T == N * L
+    s = sga or {}
+    if mode == MODE_SGA and not sga:
+        raise ValueError("SGA mode needs sga parameters")
+    if rows is None:
+        rr, nrows, rp = None, T, None
+    else:
+        rr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows, rp = rr.shape[0], _ptr(rr)
+    out = np.empty((nrows, H, d), dtype=np.float64)
+    rc = lib.vgao_attention(mode, N, L, gh, gw, H, d, dt, float(scale),
+                            _ptr(qq), _ptr(kk), _ptr(vv),
+                            s.get("stride_h", 1), s.get("stride_w", 1),
+                            s.get("phase_h", 0), s.get("phase_w", 0),
+                            s.get("diagonal", 0), s.get("mean_fill", 0),
+                            rp, nrows, _ptr(out), threads)
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return out
+
+
+def schedule(num_global, num_early, use_sga):
+    """Per-global-slot modes (MODE_FRAME / MODE_GLOBAL / MODE_SGA)."""
+    lib = _load()
+    out = np.empty(max(num_global, 0), dtype=np.int32)
+    if lib.vgao_schedule(num_global, num_early, int(bool(use_sga)), _ptr(out)) != 0:
+        raise ValueError("num_early must lie in [0, num_global]")
+    return out
+
+
+def max_threads() -> int:
+    return int(_load().vgao_max_threads())
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of raw bf16 bits to float64 (bf16 is the top half of fp32)."""
+    u = np.asarray(bits).view(np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
