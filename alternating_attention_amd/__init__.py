@@ -1,0 +1,279 @@
+"""Alternating attention for MI355X: Python binding of libvga.so.
+
+Thin argument marshalling over the C ABI declared in ``include/vga.h``:
+every step of the attention path runs in the library's HIP kernels; torch is
+used only for device memory and the current stream.  The functions keep the
+C names without the ``vga_`` prefix:
+
+* ``frame_attn(q, k, v, frames)``  -> vga_frame_attn
+* ``global_attn(q, k, v, frames)`` -> vga_global_attn
+* ``sga_attn(q, k, v, frames, sga)`` -> vga_sga_attn (+ workspace)
+* ``sga_workspace_layout(frames, sga)`` -> vga_sga_workspace_layout
+* ``layer_schedule(num_global, num_early, sga)`` -> vga_layer_schedule
+
+q, k, v: contiguous [N*L, H, 64] tensors (float32 or bfloat16) on one GPU.
+The library must be built (``alternating_attention_amd._build.build()``);
+importing this module without it raises -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvga.so")
+
+VGA_OK = 0
+STATUS_NAMES = ["VGA_OK", "VGA_ERR_NULL", "VGA_ERR_SHAPE", "VGA_ERR_DTYPE",
+                "VGA_ERR_PARAM", "VGA_ERR_ALIGN", "VGA_ERR_ALIAS",
+                "VGA_ERR_WORKSPACE", "VGA_ERR_UNSUPPORTED", "VGA_ERR_HIP"]
+VGA_F32, VGA_BF16 = 0, 1
+MODE_FRAME, MODE_GLOBAL, MODE_SGA = 0, 1, 2
+
+# every symbol include/vga.h declares
+EXPORTS = ["vga_frame_attn", "vga_global_attn", "vga_sga_workspace_layout",
+           "vga_sga_attn", "vga_layer_schedule", "vga_status_string",
+           "vga_last_error", "vga_abi_version"]
+
+
+class VgaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
+        super().__init__("%s: %s" % (name, detail))
+
+
+class CFrames(ctypes.Structure):
+    _fields_ = [("num_frames", ctypes.c_int32), ("tokens_per_frame", ctypes.c_int32),
+                ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
+                ("num_special", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+class CSga(ctypes.Structure):
+    _fields_ = [("stride_h", ctypes.c_int32), ("stride_w", ctypes.c_int32),
+                ("phase_h", ctypes.c_int32), ("phase_w", ctypes.c_int32),
+                ("diagonal", ctypes.c_int32), ("mean_fill", ctypes.c_int32)]
+
+
+class CLayer(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("sga", CSga)]
+
+
+class CLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in
+                ("keep_idx", "keep_mask", "kmean", "vmean", "kc", "vc", "partials", "total")] + \
+               [(n, ctypes.c_int64) for n in
+                ("kept_per_frame", "num_kept", "num_dropped", "partial_blocks")]
+
+
+@dataclass(frozen=True)
+class Frames:
+    """N frames of a gh x gw patch grid plus S special tokens, H heads of 64."""
+    num_frames: int
+    grid_h: int
+    grid_w: int
+    num_special: int
+    num_heads: int
+    head_dim: int = 64
+    scale: float = 0.0       # <= 0: 1/sqrt(head_dim)
+
+    @property
+    def tokens_per_frame(self) -> int:
+        return self.grid_h * self.grid_w + self.num_special
+
+    @property
+    def tokens(self) -> int:
+        return self.num_frames * self.tokens_per_frame
+
+    def c(self, dtype_code: int, tokens_per_frame: int | None = None) -> CFrames:
+        return CFrames(self.num_frames,
+                       self.tokens_per_frame if tokens_per_frame is None else tokens_per_frame,
+                       self.grid_h, self.grid_w, self.num_special, self.num_heads,
+                       self.head_dim, dtype_code, self.scale)
+
+
+@dataclass(frozen=True)
+class Sga:
+    """Subsampled Global Attention parameters (phase -1: (stride-1)//2)."""
+    stride_h: int = 2
+    stride_w: int = 2
+    phase_h: int = -1
+    phase_w: int = -1
+    diagonal: bool = True
+    mean_fill: bool = True
+
+    def c(self) -> CSga:
+        return CSga(self.stride_h, self.stride_w, self.phase_h, self.phase_w,
+                    int(self.diagonal), int(self.mean_fill))
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libvga.so is not built (%s); run "
+                          "alternating_attention_amd._build.build()" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    for name in ("vga_frame_attn", "vga_global_attn"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.POINTER(CFrames), vp, vp, vp, vp, vp]
+    lib.vga_sga_workspace_layout.restype = ctypes.c_int
+    lib.vga_sga_workspace_layout.argtypes = [ctypes.POINTER(CFrames), ctypes.POINTER(CSga),
+                                             ctypes.POINTER(CLayout)]
+    lib.vga_sga_attn.restype = ctypes.c_int
+    lib.vga_sga_attn.argtypes = [ctypes.POINTER(CFrames), ctypes.POINTER(CSga), vp, vp, vp,
+                                 vp, vp, ctypes.c_size_t, vp]
+    lib.vga_layer_schedule.restype = ctypes.c_int
+    lib.vga_layer_schedule.argtypes = [i32, i32, ctypes.POINTER(CSga), ctypes.POINTER(CLayer)]
+    lib.vga_status_string.restype = ctypes.c_char_p
+    lib.vga_status_string.argtypes = [ctypes.c_int]
+    lib.vga_last_error.restype = ctypes.c_char_p
+    lib.vga_last_error.argtypes = []
+    lib.vga_abi_version.restype = i32
+    lib.vga_abi_version.argtypes = []
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != VGA_OK:
+        raise VgaError(status, lib.vga_last_error().decode())
+
+
+def abi_version() -> int:
+    return int(lib.vga_abi_version())
+
+
+def status_string(status: int) -> str:
+    return lib.vga_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib.vga_last_error().decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return VGA_F32
+    if t.dtype == torch.bfloat16:
+        return VGA_BF16
+    raise TypeError("q/k/v must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _prepare(q, k, v, frames: Frames, out):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError("%s must be a GPU tensor" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        if t.dtype != q.dtype or t.shape != q.shape or t.device != q.device:
+            raise ValueError("q, k, v must share dtype, shape and device")
+    expect = (frames.tokens, frames.num_heads, frames.head_dim)
+    if tuple(q.shape) != expect:
+        raise ValueError("q/k/v shape %s != [N*L, H, D] = %s" % (tuple(q.shape), expect))
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous()
+          or out.device != q.device):
+        raise ValueError("out must be a contiguous tensor like q")
+    return out
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def frame_attn(q, k, v, frames: Frames, out=None):
+    """Frame attention: each token attends to the L tokens of its own frame."""
+    out = _prepare(q, k, v, frames, out)
+    cf = frames.c(_dtype_code(q))
+    _check(lib.vga_frame_attn(ctypes.byref(cf), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              out.data_ptr(), _stream(q.device)))
+    return out
+
+
+def global_attn(q, k, v, frames: Frames, out=None):
+    """Exact global attention over all N*L tokens."""
+    out = _prepare(q, k, v, frames, out)
+    cf = frames.c(_dtype_code(q))
+    _check(lib.vga_global_attn(ctypes.byref(cf), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                               out.data_ptr(), _stream(q.device)))
+    return out
+
+
+def sga_workspace_layout(frames: Frames, sga: Sga, dtype_code: int = VGA_BF16) -> CLayout:
+    cf = frames.c(dtype_code)
+    cs = sga.c()
+    lay = CLayout()
+    _check(lib.vga_sga_workspace_layout(ctypes.byref(cf), ctypes.byref(cs), ctypes.byref(lay)))
+    return lay
+
+
+def sga_attn(q, k, v, frames: Frames, sga: Sga, out=None, workspace=None):
+    """Subsampled Global Attention.  Returns (out, workspace); the workspace
+    (uint8 GPU tensor) holds keep_idx, keep_mask, kmean, vmean, Kc, Vc at the
+    offsets of ``sga_workspace_layout``."""
+    import torch
+    out = _prepare(q, k, v, frames, out)
+    code = _dtype_code(q)
+    lay = sga_workspace_layout(frames, sga, code)
+    if workspace is None or workspace.numel() < lay.total:
+        workspace = torch.empty(int(lay.total), dtype=torch.uint8, device=q.device)
+    cf = frames.c(code)
+    cs = sga.c()
+    _check(lib.vga_sga_attn(ctypes.byref(cf), ctypes.byref(cs), q.data_ptr(), k.data_ptr(),
+                            v.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+                            workspace.numel(), _stream(q.device)))
+    return out, workspace
+
+
+def workspace_views(workspace, frames: Frames, sga: Sga, dtype_code: int = VGA_BF16):
+    """Views of the SGA workspace sections (after a vga_sga_attn call)."""
+    import torch
+    lay = sga_workspace_layout(frames, sga, dtype_code)
+    H, D = frames.num_heads, frames.head_dim
+    nk, T = int(lay.num_kept), frames.tokens
+
+    def sect(off, count, dt):
+        nbytes = count * torch.tensor([], dtype=dt).element_size()
+        return workspace[off:off + nbytes].view(dt)
+
+    et = torch.float32 if dtype_code == VGA_F32 else torch.bfloat16
+    return dict(
+        keep_idx=sect(lay.keep_idx, nk, torch.int32),
+        keep_mask=sect(lay.keep_mask, T, torch.uint8),
+        kmean=sect(lay.kmean, H * D, torch.float32).view(H, D),
+        vmean=sect(lay.vmean, H * D, torch.float32).view(H, D),
+        kc=sect(lay.kc, nk * H * D, et).view(nk, H, D),
+        vc=sect(lay.vc, nk * H * D, et).view(nk, H, D),
+        layout=lay,
+    )
+
+
+def layer_schedule(num_global: int, num_early: int, sga: Sga | None):
+    """Per-global-slot list of (mode, CSga) of the training-free pipeline."""
+    arr = (CLayer * max(num_global, 1))()
+    cs = sga.c() if sga is not None else None
+    _check(lib.vga_layer_schedule(num_global, num_early,
+                                  ctypes.byref(cs) if cs is not None else None, arr))
+    return [(arr[i].mode, arr[i].sga) for i in range(num_global)]
+
+
+def attention(mode: int, q, k, v, frames: Frames, sga: Sga | None = None, out=None,
+              workspace=None):
+    """Dispatch one layer by schedule mode; returns the output tensor."""
+    if mode == MODE_FRAME:
+        return frame_attn(q, k, v, frames, out)
+    if mode == MODE_GLOBAL:
+        return global_attn(q, k, v, frames, out)
+    if mode == MODE_SGA:
+        return sga_attn(q, k, v, frames, sga, out, workspace)[0]
+    raise ValueError("unknown mode %r" % mode)

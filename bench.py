@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Benchmark of the alternating-attention hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input
+(Q, K, V resident in HBM): the layer schedule (host), one frame-attention
+layer, one exact global-attention layer and one Subsampled Global Attention
+layer (key selection, gather + mean, attention).  The default workload is
+100 frames x 1374 tokens (37x37 patches + 5 specials), 16 heads x 64, bf16.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload n100|n300|n800]
+
+Prints ONE JSON line.  `value` is tokens/s through one step (T / step time).
+Other workloads:
+  n300 -- one exact global layer vs one SGA 2x2 layer at 300 frames (speedup,
+          output deviation);
+  n800 -- the 24-slot AVGGT schedule (8 frame + 16 SGA 3x3) at 800 frames vs
+          one exact global layer timed once (x24).
+--copy-probe runs a plain 1 GiB device copy (for scaling HBM counters).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("attention tokens/s + TFLOP/s (% MFMA peak), exact vs SGA, "
+          "N=100/300/800 frames")
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E (published)
+HEAD_DIM = 64
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- work model
+def flops_global(T, H, d=HEAD_DIM):
+    """QK^T and PV: 2 * 2 * T * T * d per head."""
+    return 4.0 * T * T * d * H
+
+
+def flops_frame(N, L, H, d=HEAD_DIM):
+    return 4.0 * N * L * L * d * H
+
+
+def flops_sga(T, num_kept, H, d=HEAD_DIM):
+    return 4.0 * T * num_kept * d * H
+
+
+def bytes_gather(T, num_kept, H, d=HEAD_DIM, esize=2):
+    """Read K and V once, write the kept rows of both."""
+    return 2.0 * T * H * d * esize + 2.0 * num_kept * H * d * esize
+
+
+def attention_matrix(tokens, bytes_per_entry):
+    """(entries, bytes) of one dense tokens x tokens attention matrix."""
+    n = float(tokens) * tokens
+    return n, n * bytes_per_entry
+
+
+# ---------------------------------------------------------------- helpers
+class Timer:
+    """HIP events on the current stream (the stream the library launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def __enter__(self):
+        self.a = self.torch.cuda.Event(enable_timing=True)
+        self.b = self.torch.cuda.Event(enable_timing=True)
+        self.a.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record()
+        self.pairs.append((self.a, self.b))
+
+    def ms(self):
+        return [a.elapsed_time(b) for a, b in self.pairs]
+
+
+def cpu_baseline(workload, frames, sga_list, modes, qkv_host, rows_count, seed=7):
+    """The fp64 oracle on a bounded sample: `rows_count` seeded query rows
+    (all heads) of each mode of the step, extrapolated x T / rows."""
+    import oracle
+    q, k, v = qkv_host
+    T = frames.tokens
+    rows = np.sort(np.random.default_rng(seed).choice(T, size=rows_count, replace=False))
+    args = (frames.num_frames, frames.tokens_per_frame, frames.grid_h, frames.grid_w, 0.125)
+    t0 = time.perf_counter()
+    for mode in modes:
+        code = oracle.MODE_FRAME if mode == "frame" else oracle.MODE_GLOBAL
+        oracle.attention(code, q, k, v, *args, rows=rows)
+    for p in sga_list:
+        oracle.attention(oracle.MODE_SGA, q, k, v, *args,
+                         dict(stride_h=p.stride_h, stride_w=p.stride_w, phase_h=p.phase_h,
+                              phase_w=p.phase_w, diagonal=int(p.diagonal),
+                              mean_fill=int(p.mean_fill)), rows=rows)
+    dt = time.perf_counter() - t0
+    step_s = dt * T / rows_count
+    return {"value": T / step_s, "unit": "tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": "%d seeded query rows x %d heads of each layer of the step (%s), "
+                      "timed %.1f s, extrapolated x T/%d" % (
+                          rows_count, frames.num_heads,
+                          "+".join(list(modes) + ["sga"] * len(sga_list)), dt, rows_count),
+            "seconds_per_step": step_s}
+
+
+def host_bits(t, torch):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+# ---------------------------------------------------------------- workloads
+def run(args):
+    import torch
+    import alternating_attention_amd as vga
+    import vga_inputs
+
+    w = vga_inputs.WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    frames = vga.Frames(w.num_frames, w.grid_h, w.grid_w, w.num_special, w.num_heads)
+    T, H, N, L = frames.tokens, frames.num_heads, frames.num_frames, frames.tokens_per_frame
+    log("generating %s (T=%d)" % (w.name, T))
+    q, k, v = vga_inputs.feature_field_qkv(N, w.grid_h, w.grid_w, w.num_special, H, HEAD_DIM,
+                                           seed=w.seed, device=dev)
+    torch.cuda.synchronize()
+    out = torch.empty_like(q)
+    out_b = torch.empty_like(q)
+    timers = {}
+
+    def timed(name, fn):
+        t = timers.setdefault(name, Timer(torch))
+        with t:
+            fn()
+
+    if args.workload == "n100":
+        sga = vga.Sga(2, 2, 0, 0, True, True)
+        lay = vga.sga_workspace_layout(frames, sga)
+        ws = torch.empty(int(lay.total), dtype=torch.uint8, device=dev)
+        nk = int(lay.num_kept)
+        desc = ("N=100 frames x 1374 tokens (37x37 patches + 5 specials) = 137,400 tokens, "
+                "16 heads x 64, bf16; step = frame layer + exact global layer + SGA 2x2 layer "
+                "(phase 0, diagonal, count-weighted mean-fill)")
+
+        def step():
+            vga.layer_schedule(3, 1, sga)
+            timed("frame", lambda: vga.frame_attn(q, k, v, frames, out))
+            timed("global", lambda: vga.global_attn(q, k, v, frames, out))
+            timed("sga", lambda: vga.sga_attn(q, k, v, frames, sga, out_b, ws))
+        work = {"frame": flops_frame(N, L, H), "global": flops_global(T, H),
+                "sga": flops_sga(T, nk, H)}
+        dominant, modes, sgas = "global", ["frame", "global"], [sga]
+    elif args.workload == "n300":
+        sga = vga.Sga(2, 2, 0, 0, True, True)
+        lay = vga.sga_workspace_layout(frames, sga)
+        ws = torch.empty(int(lay.total), dtype=torch.uint8, device=dev)
+        nk = int(lay.num_kept)
+        desc = ("N=300 frames x 1374 tokens = 412,200 tokens, 16 heads x 64, bf16; "
+                "step = exact global layer + SGA 2x2 layer (phase 0, diagonal, mean-fill)")
+
+        def step():
+            timed("global", lambda: vga.global_attn(q, k, v, frames, out))
+            timed("sga", lambda: vga.sga_attn(q, k, v, frames, sga, out_b, ws))
+        work = {"global": flops_global(T, H), "sga": flops_sga(T, nk, H)}
+        dominant, modes, sgas = "global", ["global"], [sga]
+    elif args.workload == "n800":
+        sga = vga.Sga(3, 3, 1, 1, True, True)
+        lay = vga.sga_workspace_layout(frames, sga)
+        ws = torch.empty(int(lay.total), dtype=torch.uint8, device=dev)
+        nk = int(lay.num_kept)
+        plan = vga.layer_schedule(24, 8, sga)
+        desc = ("N=800 frames x 1374 tokens = 1,099,200 tokens, 16 heads x 64, bf16; "
+                "step = the 24-slot AVGGT schedule: 8 frame layers + 16 SGA 3x3 layers "
+                "(phase 1, diagonal, mean-fill); exact global layer timed once beside it")
+
+        def step():
+            for mode, cs in vga.layer_schedule(24, 8, sga):
+                if mode == vga.MODE_FRAME:
+                    timed("frame", lambda: vga.frame_attn(q, k, v, frames, out))
+                else:
+                    timed("sga", lambda: vga.sga_attn(q, k, v, frames, sga, out_b, ws))
+        work = {"frame": 8 * flops_frame(N, L, H), "sga": 16 * flops_sga(T, nk, H)}
+        dominant, modes, sgas = "sga", ["frame"], [sga]
+        assert len(plan) == 24
+    else:
+        raise SystemExit("unknown workload")
+
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timers.clear()
+    log("timing %d steps" % args.steps)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step()
+        log("  step %d enqueued" % i)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+
+    per = {}
+    for name, t in timers.items():
+        ms = t.ms()
+        calls_per_step = len(ms) / args.steps
+        avg = float(np.mean(ms))
+        flop = work[name] / calls_per_step
+        per[name] = {"ms_per_call": avg, "calls_per_step": calls_per_step,
+                     "tflops": flop / (avg * 1e-3) / 1e12,
+                     "frac_mfma_peak": flop / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                     "tokens_per_s": T / (avg * 1e-3)}
+    if "sga" in per:
+        gb = bytes_gather(T, nk, H)
+        per["sga"]["gather_bytes"] = gb
+        per["sga"]["kept_per_frame"] = int(lay.kept_per_frame)
+
+    extra = {}
+    if args.workload in ("n300", "n800"):
+        if args.workload == "n800":
+            log("exact global layer, timed once")
+            g = Timer(torch)
+            with g:
+                vga.global_attn(q, k, v, frames, out)
+            torch.cuda.synchronize()
+            gms = g.ms()[0]
+            per["global_once"] = {"ms_per_call": gms,
+                                  "tflops": flops_global(T, H) / (gms * 1e-3) / 1e12,
+                                  "frac_mfma_peak": flops_global(T, H) / (gms * 1e-3) / 1e12
+                                  / PEAK_BF16_TFLOPS}
+            extra["schedule_vs_24_exact_speedup"] = 24 * gms / ms_step
+            extra["sga_vs_exact_layer_speedup"] = gms / per["sga"]["ms_per_call"]
+        else:
+            extra["sga_vs_exact_layer_speedup"] = (per["global"]["ms_per_call"]
+                                                   / per["sga"]["ms_per_call"])
+        # deviation of SGA from exact attention (both from the GPU)
+        vga.global_attn(q, k, v, frames, out)
+        vga.sga_attn(q, k, v, frames, sga, out_b, ws)
+        torch.cuda.synchronize()
+        dev_ = (out_b.float() - out.float())
+        extra["sga_deviation"] = {"max_abs": float(dev_.abs().max()),
+                                  "mean_abs": float(dev_.abs().mean()),
+                                  "rel_l2": float(dev_.norm() / out.float().norm())}
+
+    flop_dom = work[dominant] / per[dominant]["calls_per_step"]
+    ach = flop_dom / (per[dominant]["ms_per_call"] * 1e-3) / 1e12
+    kernel = {"global": "flash_bf16_kernel<kGlobal>", "sga": "flash_bf16_kernel<kSga>"}[dominant]
+    roofline = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / PEAK_BF16_TFLOPS, "traffic": None, "kernel": kernel,
+                "algorithmic_flops_per_launch": flop_dom}
+
+    result = {
+        "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded shifted-feature-field tokens projected by seeded random "
+                "weights (no dataset, no trained weights)",
+        "config": {"workload": desc, "frames": N, "tokens_per_frame": L, "tokens": T,
+                   "heads": H, "head_dim": HEAD_DIM},
+        "roofline": roofline, "modes": per, "wall_s_timed": wall,
+    }
+    result.update(extra)
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle, %d rows per layer)" % args.cpu_rows)
+        qkv = (host_bits(q, torch), host_bits(k, torch), host_bits(v, torch))
+        result["cpu_baseline"] = cpu_baseline(w, frames, sgas, modes, qkv, args.cpu_rows)
+    return result
+
+
+def copy_probe():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "copies": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="n100", choices=["n100", "n300", "n800"])
+    ap.add_argument("--cpu-rows", type=int, default=96)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the multi-GPU sharding of this path is a "
+              "design, not a build (see the design notes); use --gpus 1", file=sys.stderr)
+        raise SystemExit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
+    defaults = {"n100": (10, 2), "n300": (3, 1), "n800": (1, 1)}[args.workload]
+    args.steps = args.steps if args.steps is not None else defaults[0]
+    args.warmup = args.warmup if args.warmup is not None else defaults[1]
+    res = run(args)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,167 @@
+/*
+ * vga.h -- C ABI of the alternating-attention library (libvga.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation set follows two pages:
+ *  - "VGGT CVPR25 Best Paper" notes, section "Alternating-Attention": a
+ *    trunk that alternates frame-wise self-attention (each frame's tokens
+ *    attend to their own frame) with global self-attention (every token of
+ *    every frame attends to all N*L tokens); the N*L x N*L matrix must never
+ *    be materialised (FlashAttention remark in the same section).
+ *  - "AVGGT: Rethinking Global Attention for Accelerating VGGT", technical
+ *    summary, section 3 (Methodology): step one converts the early global
+ *    layers to frame attention; step two, Subsampled Global Attention (SGA),
+ *    keeps every query, keeps K/V only on a strided s_h x s_w patch grid
+ *    (plus the special tokens), keeps each token's own diagonal term,
+ *    replaces all dropped K/V columns by one global mean column, and puts
+ *    the three parts under one shared softmax.
+ *
+ * Tensor layout (all calls): Q, K, V and O are contiguous device arrays of
+ * shape [T, H, D] with T = N * L tokens, token-major and frame-major: token
+ * t = f * L + u belongs to frame f; inside a frame the gh*gw patch tokens
+ * come first in row-major grid order (u = r * gw + c), then the S special
+ * tokens (u >= gh*gw).  D (head_dim) must be 64.  The element type is fp32
+ * or bf16 for all four arrays of one call; accumulation is always fp32.
+ *
+ * Conventions for every call:
+ *  - Ownership: the caller allocates and frees every device buffer (Q, K, V,
+ *    O, workspace).  The library allocates no device memory and keeps no
+ *    pointer after it returns.
+ *  - Asynchrony: work is only enqueued on `stream` (a hipStream_t; NULL is
+ *    the default stream).  No call synchronises the host, except when the
+ *    environment variable VGA_DEBUG_SYNC=1 is set (then each call waits for
+ *    its own work and reports asynchronous faults as VGA_ERR_HIP).
+ *  - Errors: a status code, never an exception.  All argument checks run
+ *    before anything is enqueued, so a failing call enqueues nothing;
+ *    vga_last_error() gives a thread-local text for the last failure.
+ *  - Requirements: Q/K/V/O (and the workspace) 16-byte aligned; O must not
+ *    overlap Q, K, V or the workspace; each array at most 2^31 elements.
+ *  - Thread safety: all calls are stateless and may run concurrently on
+ *    different streams.
+ */
+#ifndef VGA_H
+#define VGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VGA_ABI_VERSION 1
+
+typedef enum {
+  VGA_OK = 0,
+  VGA_ERR_NULL = 1,        /* a required pointer is NULL                    */
+  VGA_ERR_SHAPE = 2,       /* inconsistent N, L, grid, S, H or size limit   */
+  VGA_ERR_DTYPE = 3,       /* dtype is not VGA_F32 / VGA_BF16               */
+  VGA_ERR_PARAM = 4,       /* bad SGA stride/phase/flag or schedule counts  */
+  VGA_ERR_ALIGN = 5,       /* a device pointer is not 16-byte aligned       */
+  VGA_ERR_ALIAS = 6,       /* O overlaps an input or the workspace          */
+  VGA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than required       */
+  VGA_ERR_UNSUPPORTED = 8, /* head_dim != 64                                */
+  VGA_ERR_HIP = 9          /* the HIP runtime reported an error             */
+} vga_status;
+
+typedef enum { VGA_F32 = 0, VGA_BF16 = 1 } vga_dtype;
+
+/* Shape of Q/K/V/O: N frames of L = grid_h*grid_w + num_special tokens. */
+typedef struct {
+  int32_t num_frames;       /* N >= 1                                        */
+  int32_t tokens_per_frame; /* L; must equal grid_h*grid_w + num_special     */
+  int32_t grid_h, grid_w;   /* patch grid, e.g. 37 x 37 for 518px / 14px    */
+  int32_t num_special;      /* S >= 0, stored after the patches of a frame   */
+  int32_t num_heads;        /* H >= 1                                        */
+  int32_t head_dim;         /* D; must be 64                                 */
+  int32_t dtype;            /* vga_dtype of Q, K, V and O                    */
+  float scale;              /* softmax scale; <= 0 selects 1/sqrt(head_dim)  */
+} vga_frames;
+
+/* Subsampled Global Attention parameters (AVGGT, section 3, step two).
+ * Patch (r, c) of every frame is kept as a K/V column iff
+ * r mod stride_h == phase_h and c mod stride_w == phase_w; the special
+ * tokens are always kept.  A truncated window at the grid edge gets no extra
+ * sample.  The kept-per-frame count is
+ *   kpf = S + ceil((gh - phase_h) / stride_h) * ceil((gw - phase_w) / stride_w). */
+typedef struct {
+  int32_t stride_h, stride_w; /* 1..grid_h, 1..grid_w                        */
+  int32_t phase_h, phase_w;   /* 0..stride-1; -1 selects (stride - 1) / 2    */
+  int32_t diagonal;  /* 0/1: add the query's own (k_i, v_i) column iff its
+                        token was dropped (never counted twice)             */
+  int32_t mean_fill; /* 0/1: add one column with key kmean and value vmean
+                        (means over all |D| dropped tokens, per head) whose
+                        logit is scale*<q,kmean> + ln|D|, i.e. it weighs as
+                        |D| copies; absent when |D| == 0                     */
+} vga_sga;
+
+typedef enum { VGA_MODE_FRAME = 0, VGA_MODE_GLOBAL = 1, VGA_MODE_SGA = 2 } vga_mode;
+
+typedef struct {
+  int32_t mode;  /* vga_mode                                                 */
+  vga_sga sga;   /* meaningful when mode == VGA_MODE_SGA (phases resolved)   */
+} vga_layer;
+
+/* Byte offsets of the SGA workspace sections (each 256-byte aligned) and
+ * the selection sizes.  The workspace holds, after vga_sga_attn:
+ *   keep_idx  int32 [num_kept]   kept token indices, ascending
+ *   keep_mask uint8 [T]          1 iff the token is kept
+ *   kmean     fp32  [H, 64]      mean key over the dropped tokens
+ *   vmean     fp32  [H, 64]      mean value over the dropped tokens
+ *   kc, vc    dtype [num_kept, H, 64]  the kept K and V rows, compacted
+ *   partials  fp32  [partial_blocks, 2, H, 64]  per-block dropped sums   */
+typedef struct {
+  uint64_t keep_idx, keep_mask, kmean, vmean, kc, vc, partials;
+  uint64_t total;           /* bytes the workspace must hold               */
+  int64_t kept_per_frame;   /* kpf                                         */
+  int64_t num_kept;         /* N * kpf                                     */
+  int64_t num_dropped;      /* |D| = T - N * kpf                           */
+  int64_t partial_blocks;   /* number of partial-sum blocks                */
+} vga_sga_ws_layout;
+
+/* Frame attention ("VGGT CVPR25 Best Paper" notes, "Alternating-Attention";
+ * AVGGT section 3, step one): for every frame f, head h and token i of f,
+ *   O[i,h] = softmax_j(scale * <Q[i,h], K[j,h]>) V[j,h]
+ * over the L tokens j of frame f (specials included).
+ * Returns VGA_OK or an error status; nothing is enqueued on error. */
+vga_status vga_frame_attn(const vga_frames* shape, const void* q, const void* k,
+                          const void* v, void* o, void* stream);
+
+/* Exact global attention (same section): as above with j over all T
+ * tokens of all frames; the T x T matrix is never written to memory. */
+vga_status vga_global_attn(const vga_frames* shape, const void* q, const void* k,
+                           const void* v, void* o, void* stream);
+
+/* Fills *out with the SGA workspace layout for (shape, sga) -- host only,
+ * no device work.  Returns VGA_OK or the same validation errors as
+ * vga_sga_attn. */
+vga_status vga_sga_workspace_layout(const vga_frames* shape, const vga_sga* sga,
+                                    vga_sga_ws_layout* out);
+
+/* Subsampled Global Attention (AVGGT section 3, step two).  For every token
+ * i and head h, one softmax over: the kept columns (keep_idx), the own column
+ * (k_i, v_i) iff diagonal and token i was dropped, and the mean column iff
+ * mean_fill and |D| > 0.  workspace: device buffer of at least
+ * vga_sga_workspace_layout().total bytes, owned by the caller; its sections
+ * are rewritten by every call. */
+vga_status vga_sga_attn(const vga_frames* shape, const vga_sga* sga, const void* q,
+                        const void* k, const void* v, void* o, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Per-layer schedule of the training-free pipeline (AVGGT section 3):
+ * slot g < num_early_to_frame becomes VGA_MODE_FRAME; the remaining slots
+ * are VGA_MODE_SGA with *sga (phases resolved), or VGA_MODE_GLOBAL when sga
+ * is NULL.  out: host array of num_global_layers entries.  Host only.
+ * Errors: VGA_ERR_NULL (out NULL with num_global_layers > 0), VGA_ERR_PARAM
+ * (counts out of range or bad SGA strides/phases/flags). */
+vga_status vga_layer_schedule(int32_t num_global_layers, int32_t num_early_to_frame,
+                              const vga_sga* sga, vga_layer* out);
+
+const char* vga_status_string(vga_status status);
+const char* vga_last_error(void); /* thread-local detail of the last failure */
+int32_t vga_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VGA_H */

@@ -1,0 +1,155 @@
+"""Host-side checks of libvga.so (CPU only: no kernel is launched).
+
+* the library loads and exports every function include/vga.h declares;
+* argument validation rejects bad calls with the documented status before
+  anything would be enqueued (fake, never-dereferenced device pointers);
+* the SGA workspace layout reports the closed-form kept counts;
+* the layer schedule.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.oracle_pins import kept_per_frame_closed_form
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def vga():
+    import alternating_attention_amd as vga
+    return vga
+
+
+def _declared():
+    hdr = open(os.path.join(ROOT, "include", "vga.h")).read()
+    hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
+    return sorted(set(re.findall(r"\b(vga_[a-z_]+)\s*\(", hdr)))
+
+
+def test_exports_every_declared_symbol(vga):
+    declared = _declared()
+    assert declared == sorted(vga.EXPORTS)
+    raw = ctypes.CDLL(vga.LIB_PATH)
+    for name in declared:
+        assert getattr(raw, name) is not None, name
+
+
+def test_abi_version_and_strings(vga):
+    assert vga.abi_version() == 1
+    for code, name in enumerate(vga.STATUS_NAMES):
+        assert vga.status_string(code) == name
+
+
+def _frames(vga, **kw):
+    f = dict(num_frames=2, grid_h=8, grid_w=8, num_special=5, num_heads=2)
+    f.update(kw)
+    return vga.Frames(**f)
+
+
+FAKE = 0x7F0000000000  # 16-byte aligned; never dereferenced by validation
+
+
+def _call_global(vga, cf, q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000,
+                 o=FAKE + 0x3000000):
+    return vga.lib.vga_global_attn(ctypes.byref(cf), q, k, v, o, None)
+
+
+def test_validation_statuses(vga):
+    f = _frames(vga)
+    ok = f.c(vga.VGA_BF16)
+    # NULL pointers
+    assert vga.lib.vga_global_attn(None, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert _call_global(vga, ok, q=None) == 1
+    assert "non-NULL" in vga.last_error()
+    # L inconsistent with grid + specials
+    assert _call_global(vga, f.c(vga.VGA_BF16, tokens_per_frame=70)) == 2
+    # dtype
+    bad = f.c(vga.VGA_BF16)
+    bad.dtype = 7
+    assert _call_global(vga, bad) == 3
+    # head_dim
+    bad = f.c(vga.VGA_BF16)
+    bad.head_dim = 128
+    assert _call_global(vga, bad) == 8
+    # alignment
+    assert _call_global(vga, ok, k=FAKE + 8) == 5
+    # o aliases q
+    assert _call_global(vga, ok, o=FAKE + 64) == 6
+    # too large: T*H*64 >= 2^31
+    big = vga.Frames(num_frames=20000, grid_h=37, grid_w=37, num_special=5, num_heads=16)
+    assert _call_global(vga, big.c(vga.VGA_BF16)) == 2
+    # frame attention shares the checks
+    assert vga.lib.vga_frame_attn(ctypes.byref(ok), None, FAKE, FAKE, FAKE, None) == 1
+
+
+def test_sga_validation(vga):
+    f = _frames(vga)
+    cf = f.c(vga.VGA_BF16)
+
+    def call(sga, ws=FAKE + 0x4000000, nbytes=1 << 30, o=FAKE + 0x3000000):
+        cs = sga.c()
+        return vga.lib.vga_sga_attn(ctypes.byref(cf), ctypes.byref(cs), FAKE,
+                                    FAKE + 0x1000000, FAKE + 0x2000000, o, ws, nbytes, None)
+
+    assert call(vga.Sga(stride_h=0)) == 4                  # stride < 1
+    assert call(vga.Sga(stride_h=9)) == 4                  # stride > grid
+    assert call(vga.Sga(stride_h=2, phase_h=2)) == 4       # phase >= stride
+    assert call(vga.Sga(diagonal=2)) == 4
+    assert call(vga.Sga(), ws=None) == 7
+    assert call(vga.Sga(), nbytes=100) == 7
+    assert call(vga.Sga(), ws=FAKE + 0x4000008) == 5
+    assert call(vga.Sga(), ws=FAKE + 0x3000000 + 256) == 6  # o overlaps workspace
+    assert vga.lib.vga_sga_attn(ctypes.byref(cf), None, FAKE, FAKE, FAKE, FAKE, FAKE, 1,
+                                None) == 1
+
+
+@pytest.mark.parametrize("gh,gw,S,sh,sw,oh,ow", [
+    (8, 8, 5, 2, 2, 0, 0), (37, 37, 5, 2, 2, 0, 0), (37, 37, 5, 3, 3, 1, 1),
+    (37, 37, 5, 3, 3, -1, -1), (5, 7, 2, 3, 2, 2, 1), (6, 4, 0, 1, 1, 0, 0),
+    (1, 1, 0, 1, 1, 0, 0), (9, 3, 4, 4, 3, 3, 2)])
+def test_workspace_layout_counts(vga, gh, gw, S, sh, sw, oh, ow):
+    N = 3
+    f = vga.Frames(num_frames=N, grid_h=gh, grid_w=gw, num_special=S, num_heads=4)
+    lay = vga.sga_workspace_layout(f, vga.Sga(sh, sw, oh, ow))
+    rh = (sh - 1) // 2 if oh == -1 else oh
+    rw = (sw - 1) // 2 if ow == -1 else ow
+    kpf = kept_per_frame_closed_form(gh, gw, S, sh, sw, rh, rw)
+    assert lay.kept_per_frame == kpf
+    assert lay.num_kept == N * kpf
+    assert lay.num_dropped == f.tokens - N * kpf
+    offs = [lay.keep_idx, lay.keep_mask, lay.kmean, lay.vmean, lay.kc, lay.vc, lay.partials]
+    assert all(o % 256 == 0 for o in offs)
+    assert offs == sorted(offs) and lay.total >= lay.partials + 8 * 4 * 64 * lay.partial_blocks
+
+
+def test_kept_counts_of_the_workloads(vga):
+    # 8x8 + 5 at 2x2 -> 21 per frame; 37x37 + 5 at 2x2 -> 366; at 3x3 phase 1 -> 149
+    for (g, s, ph, kpf) in [(8, 2, 0, 21), (37, 2, 0, 366), (37, 3, 1, 149)]:
+        f = vga.Frames(num_frames=2, grid_h=g, grid_w=g, num_special=5, num_heads=16)
+        lay = vga.sga_workspace_layout(f, vga.Sga(s, s, ph, ph))
+        assert lay.kept_per_frame == kpf
+
+
+def test_layer_schedule(vga):
+    sch = vga.layer_schedule(24, 8, vga.Sga(3, 3, -1, -1))
+    assert [m for m, _ in sch] == [vga.MODE_FRAME] * 8 + [vga.MODE_SGA] * 16
+    assert all(s.phase_h == 1 and s.phase_w == 1 and s.diagonal == 1 for m, s in sch[8:])
+    sch = vga.layer_schedule(6, 2, None)
+    assert [m for m, _ in sch] == [vga.MODE_FRAME] * 2 + [vga.MODE_GLOBAL] * 4
+    with pytest.raises(vga.VgaError) as ei:
+        vga.layer_schedule(4, 5, None)
+    assert ei.value.status == 4
+    with pytest.raises(vga.VgaError):
+        vga.layer_schedule(4, 1, vga.Sga(stride_h=0))
+    assert vga.lib.vga_layer_schedule(3, 1, None, None) == 1
+    assert vga.layer_schedule(0, 0, None) == []
+
+
+def test_schedule_matches_oracle(vga):
+    import oracle
+    for G, E, use in [(24, 8, True), (12, 0, False), (5, 5, True)]:
+        mine = [m for m, _ in vga.layer_schedule(G, E, vga.Sga() if use else None)]
+        assert mine == list(oracle.schedule(G, E, use))
