@@ -20,20 +20,24 @@
 // operand without touching LDS.  K rows are stored in LDS in a permuted
 // order (bits 2 and 3 of the row index swapped) so that accumulator
 // register r of lane half h holds key 16*(r/8) + 8*h + r%8 -- exactly the
-// B-operand k-slot order of the PV product.  V is stored transposed (V^T,
-// keys contiguous) so the PV A operand is one 16-byte LDS read.  Both LDS
-// tiles use XOR-swizzled 16-byte chunks to avoid bank conflicts.
+// B-operand k-slot order of the PV product.  V stays in its natural layout;
+// the PV A operand (V^T) comes from ds_read_b64_tr_b16 transposed reads.
+// K/V tiles move global -> LDS with global_load_lds_dwordx4 (no registers),
+// double buffered: tile t+1 loads while tile t is computed.
 //
 // Softmax: the MFMA produces exact fp32 dot products of the bf16 rows; one
 // FMA per score turns them into log2 units and subtracts the row's
-// reference max m.  The reference max is updated lazily: a tile whose probabilities sum above
-// 2^16 in a lane (or the first tile) takes a wave-uniform slow path that
-// raises m to the tile max and rescales O and l; otherwise P = exp2(S)
-// directly.  P is rounded to bf16 (RNE) for the PV MFMA; l, O accumulate in
-// fp32.
+// reference max m.  m is updated lazily: the first tile, or a tile whose
+// probabilities sum above 2^16 in a lane, takes a wave-uniform slow path
+// that recomputes S, raises m to the tile max and rescales O and l (the
+// textbook online softmax); every other tile uses P = exp2(S - m) as is.
+// P is rounded to bf16 (RNE) for the PV MFMA; l (summed from the rounded P)
+// and O accumulate in fp32.
 //
 // fp32 path: a plain VALU kernel (one lane per query and head, exact online
 // softmax in fp32), used for fp32 inputs.
+#include <type_traits>
+
 #include "vga_internal.h"
 
 namespace vga {
@@ -69,12 +73,6 @@ __device__ __forceinline__ int perm_row(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
-// Element offset of 16-byte chunk j of K row i in a [64][64] bf16 tile.
-__device__ __forceinline__ int k_off(int row, int j) { return row * 64 + ((j ^ (row & 7)) << 3); }
-// Element offset of key-chunk kc (8 keys) of V^T row d in a [64][64] tile.
-__device__ __forceinline__ int v_off(int d, int kc) {
-  return d * 64 + ((kc ^ ((d ^ (d >> 3)) & 7)) << 3);
-}
 
 struct TileRange {
   int64_t q_begin, q_end;    // query rows of this workgroup
@@ -115,10 +113,27 @@ __device__ __forceinline__ bool sga_kept(const SgaGrid& g, int64_t t) {
   return (r % g.sh == g.oh) && (c % g.sw == g.ow);
 }
 
+// LDS tiles.  K: 64 rows of 128 bytes padded to 144 (row i of a 32-key
+// sub-tile holds key perm_row(i)); V: 64 rows (natural key order) padded to
+// 160 bytes.  The padding spreads the rows that one LDS read touches over
+// distinct banks, and keeps every read address a per-lane base plus an
+// immediate.  Both tiles are filled by global_load_lds_dwordx4 (global ->
+// LDS without registers), 1 KB (64 x 16 bytes) per instruction; granules
+// that fall in the padding load a harmless in-range duplicate.
+constexpr int kKRow = 144, kVRow = 160;
+constexpr int kKTile = kBK * kKRow, kVTile = kBK * kVRow;     // 9216, 10240
+constexpr int kStage = kKTile + kVTile;                        // 19456
+constexpr int kKInstr = kKTile / 1024, kVInstr = kVTile / 1024;  // 9, 10
+constexpr int kDmaSlots = (kKInstr + kVInstr + 3) / 4;         // per wave: 5
+constexpr int kStages = 2;
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
 template <KeyRange KR>
 __global__ void __launch_bounds__(kThreads, 2) flash_bf16_kernel(FlashParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kBK * 64];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][64 * kBK];
+  __shared__ __attribute__((aligned(16))) char lds[kStages * kStage];
 
   const TileRange tr = tile_range<KR>(p);
   const int tid = threadIdx.x;
@@ -129,21 +144,17 @@ __global__ void __launch_bounds__(kThreads, 2) flash_bf16_kernel(FlashParams p) 
   const int H = p.H;
   const int head = tr.head;
   const uint16_t* __restrict__ qg = (const uint16_t*)p.q;
-  const uint16_t* __restrict__ kg = (const uint16_t*)p.k;
-  const uint16_t* __restrict__ vg = (const uint16_t*)p.v;
   const float qscale = p.scale * kLog2e;
+  const int64_t row_bytes = (int64_t)H * 128;
 
   // ---- Q block of this wave into registers (B operand of S^T = K Q^T):
-  // lane holds query l32 of block qb, dims 16c + 8*hf + [0, 8), as stored.
+  // lane holds query l32 of block qb (clamped into range), dims
+  // 16c + 8*hf + [0, 8), as stored.
   bf16x8 qreg[2][4];
-  int64_t qrow[2];
-  bool qvalid[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int64_t row = tr.q_begin + wave * kQPerWave + qb * 32 + l32;
-    qvalid[qb] = row < tr.q_end;
-    qrow[qb] = qvalid[qb] ? row : tr.q_end - 1;
-    const uint16_t* src = qg + ((size_t)qrow[qb] * H + head) * 64 + 8 * hf;
+    const int64_t row = min(tr.q_begin + wave * kQPerWave + qb * 32 + l32, tr.q_end - 1);
+    const uint16_t* src = qg + ((size_t)row * H + head) * 64 + 8 * hf;
 #pragma unroll
     for (int c = 0; c < 4; ++c) qreg[qb][c] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + 16 * c));
   }
@@ -169,7 +180,7 @@ __global__ void __launch_bounds__(kThreads, 2) flash_bf16_kernel(FlashParams p) 
     const uint16_t* vf = (const uint16_t*)p.v_full;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const int64_t row = qrow[qb];
+      const int64_t row = min(tr.q_begin + wave * kQPerWave + qb * 32 + l32, tr.q_end - 1);
       const bool diag = p.use_diag && !sga_kept(p.grid, row);
       const uint16_t* qs = qg + ((size_t)row * H + head) * 64 + 8 * hf;
       const uint16_t* ks = kf + ((size_t)row * H + head) * 64 + 8 * hf;
@@ -220,67 +231,97 @@ __global__ void __launch_bounds__(kThreads, 2) flash_bf16_kernel(FlashParams p) 
     }
   }
 
-  // ---- K/V tile staging: global -> registers -> LDS (double buffered).
-  const int ld_j = tid & 7;    // 16-byte chunk (8 dims) of a row
-  const int ld_i = tid >> 3;   // 0..31
-  u32x4 kst[2], vst[2];
-  auto load_tile = [&](int64_t key0) {
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int64_t kk = key0 + 32 * rr + perm_row(ld_i);
-      kst[rr] = kk < tr.k_end
-                    ? *(const u32x4*)(kg + ((size_t)kk * H + head) * 64 + 8 * ld_j)
-                    : u32x4{0u, 0u, 0u, 0u};
-      const int64_t kv = key0 + 2 * ld_i + rr;
-      vst[rr] = kv < tr.k_end
-                    ? *(const u32x4*)(vg + ((size_t)kv * H + head) * 64 + 8 * ld_j)
-                    : u32x4{0u, 0u, 0u, 0u};
+  // ---- DMA plan: wave w issues the tile's 1 KB instructions w, w+4, ...
+  // (0..8: K, 9..18: V).  A lane's granule: key offset within the tile and
+  // byte offset within the row.
+  auto dma_granule = [&](int i, int& key, uint32_t& col) {
+    if (i < kKInstr) {
+      const int g = i * 64 + lane, row = g / 9, gc = g % 9;
+      key = (row & 32) + perm_row(row & 31);
+      col = gc < 8 ? gc * 16 : 0;
+    } else {
+      const int g = (i - kKInstr) * 64 + lane, row = g / 10, gc = g % 10;
+      key = row;
+      col = gc < 8 ? gc * 16 : 0;
     }
   };
-  auto store_tile = [&](int st) {
+  uint32_t dma_off[kDmaSlots];
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int row = 32 * rr + ld_i;
-      *(u32x4*)&lds_k[st][k_off(row, ld_j)] = kst[rr];
-    }
-    // V^T: dims 8*ld_j + e, keys 2*ld_i and 2*ld_i + 1 packed in one word
-    const int key = 2 * ld_i;
+  for (int s = 0; s < kDmaSlots; ++s) {
+    int key;
+    uint32_t col;
+    dma_granule(4 * s + wave, key, col);
+    dma_off[s] = (uint32_t)key * (uint32_t)row_bytes + col;
+  }
+  const char* kbytes = (const char*)p.k + (int64_t)head * 128;
+  const char* vbytes = (const char*)p.v + (int64_t)head * 128;
+  // Issue the DMA of the tile at key0 into `stage`; with clamp (ragged last
+  // tile) keys past the range load the last key instead.
+  auto issue = [&](int64_t key0, int stage, auto clamp_tag) {
+    constexpr bool clamp = decltype(clamp_tag)::value;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 8 * ld_j + e;
-      const uint32_t a = vst[0][e >> 1], b = vst[1][e >> 1];
-      const uint32_t w = (e & 1) ? __builtin_amdgcn_perm(b, a, 0x07060302u)
-                                 : __builtin_amdgcn_perm(b, a, 0x05040100u);
-      *(uint32_t*)&lds_v[st][v_off(d, key >> 3) + (key & 7)] = w;
+    for (int s = 0; s < kDmaSlots; ++s) {
+      const int i = 4 * s + wave;
+      if (i >= kKInstr + kVInstr) continue;
+      const bool isk = i < kKInstr;
+      const char* base = isk ? kbytes : vbytes;
+      const char* src;
+      if constexpr (clamp) {
+        int kk;
+        uint32_t col;
+        dma_granule(i, kk, col);
+        int64_t key = key0 + kk;
+        key = key < tr.k_end ? key : tr.k_end - 1;
+        src = base + key * row_bytes + col;
+      } else {
+        src = base + key0 * row_bytes + dma_off[s];
+      }
+      char* dst = lds + stage * kStage + (isk ? i * 1024 : kKTile + (i - kKInstr) * 1024);
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
   };
 
-  const int64_t ntiles = (tr.k_end - tr.k_begin + kBK - 1) / kBK;
+  // per-lane LDS read bases: K operand (row l32 of a sub-tile, granule hf)
+  // and the V^T transposed read (16-lane group g reads 4 keys x 16 dims).
+  const int kread = l32 * kKRow + hf * 16;
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int vread = kKTile + (8 * hf + (j16 >> 2)) * kVRow + (16 * (g16 & 1) + 4 * (j16 & 3)) * 2;
 
-  load_tile(tr.k_begin);
-  store_tile(0);
-  __syncthreads();
+  const int64_t nkeys = tr.k_end - tr.k_begin;
+  const int64_t nfull = nkeys / kBK;
+  const int64_t ntiles = (nkeys + kBK - 1) / kBK;
+  const bf16x2 kOnes = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 
-  for (int64_t t = 0; t < ntiles; ++t) {
+  // One key tile.  Full tiles run without any masking; a ragged last tile
+  // (tail) runs the same body with its out-of-range keys masked to -inf.
+  auto tile_step = [&](int64_t t, auto tail_tag) {
+    constexpr bool tail = decltype(tail_tag)::value;
     const int st = (int)(t & 1);
     const int64_t key0 = tr.k_begin + t * kBK;
-    if (t + 1 < ntiles) load_tile(key0 + kBK);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA landed
+    __syncthreads();                     // ... and every other wave's
+    if (t + 1 < ntiles) {
+      if (t + 1 == nfull)
+        issue(key0 + kBK, st ^ 1, std::true_type{});
+      else
+        issue(key0 + kBK, st ^ 1, std::false_type{});
+    }
+    const char* sk = lds + st * kStage + kread;
+    const char* sv = lds + st * kStage + vread;
 
     // ---- S^T = scale*log2(e) * K Q^T - m for block qb and 32-key sub-tile
-    // sb, with the keys past the end of the range masked to -inf.
+    // sb; keys past the end of the range (tail tile only) get -inf.
     auto scores = [&](int qb, int sb) {
-      const int row = 32 * sb + l32;
       f32x16 acc = 0.f;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const bf16x8 ka = __builtin_bit_cast(
-            bf16x8, *(const u32x4*)&lds_k[st][k_off(row, 2 * c + hf)]);
+        const bf16x8 ka = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(sk + sb * 32 * kKRow + c * 32));
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[qb][c], acc, 0, 0, 0);
       }
       const float nm = -m[qb];
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] = __builtin_fmaf(acc[r], qscale, nm);
-      if (key0 + kBK > tr.k_end) {
+      if constexpr (tail) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t key = key0 + 32 * sb + 16 * (r >> 3) + 8 * hf + (r & 7);
@@ -291,16 +332,15 @@ __global__ void __launch_bounds__(kThreads, 2) flash_bf16_kernel(FlashParams p) 
     };
     // P = exp2(S - delta) rounded to bf16 into the PV operand; returns the
     // lane's fp32 sum of the rounded P (the values the PV product uses).
-    const bf16x2 kOnes = __builtin_bit_cast(bf16x2, 0x3f803f80u);
     u32x4 pk[2][2][2];  // [qb][sb][k-chunk] bf16 P^T operands
-    auto exp_pack = [&](int qb, int sb, const f32x16& sv, float delta) {
+    auto exp_pack = [&](int qb, int sb, const f32x16& sv2, float delta) {
       float acc = 0.f;
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(sv[8 * c2 + 2 * e] - delta);
-          const float p1 = __builtin_amdgcn_exp2f(sv[8 * c2 + 2 * e + 1] - delta);
+          const float p0 = __builtin_amdgcn_exp2f(sv2[8 * c2 + 2 * e] - delta);
+          const float p1 = __builtin_amdgcn_exp2f(sv2[8 * c2 + 2 * e + 1] - delta);
           const uint32_t pp = pack_bf16(p0, p1);
           pk[qb][sb][c2][e] = pp;
           acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), kOnes, acc, false);
@@ -313,9 +353,9 @@ __global__ void __launch_bounds__(kThreads, 2) flash_bf16_kernel(FlashParams p) 
     bool slow = (t == 0);
     if (!slow) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) lt[qb] += exp_pack(qb, sb, scores(qb, sb), 0.f);
+        for (int qb = 0; qb < 2; ++qb) lt[qb] += exp_pack(qb, sb, scores(qb, sb), 0.f);
       slow = __any(!(lt[0] <= kRescaleSum && lt[1] <= kRescaleSum));
     }
     // ---- slow path (first tile, or a tile far above the reference max):
@@ -323,12 +363,12 @@ __global__ void __launch_bounds__(kThreads, 2) flash_bf16_kernel(FlashParams p) 
     if (slow) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        f32x16 sv[2] = {scores(qb, 0), scores(qb, 1)};
+        f32x16 sv2[2] = {scores(qb, 0), scores(qb, 1)};
         float mx = -INFINITY;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[sb][r]);
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv2[sb][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float delta = mset[qb] ? fmaxf(mx, 0.f) : mx;
         const float factor = mset[qb] ? exp2f(-delta) : 1.f;
@@ -337,32 +377,35 @@ __global__ void __launch_bounds__(kThreads, 2) flash_bf16_kernel(FlashParams p) 
         lsum[qb] *= factor;
         o[qb][0] *= factor;
         o[qb][1] *= factor;
-        lt[qb] = exp_pack(qb, 0, sv[0], delta) + exp_pack(qb, 1, sv[1], delta);
+        lt[qb] = exp_pack(qb, 0, sv2[0], delta) + exp_pack(qb, 1, sv2[1], delta);
       }
     }
     lsum[0] += lt[0];
     lsum[1] += lt[1];
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T; the V^T operand comes from two transposed reads
 #pragma unroll
-    for (int db = 0; db < 2; ++db) {
-      const int d = 32 * db + l32;
+    for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
-          const bf16x8 va = __builtin_bit_cast(
-              bf16x8, *(const u32x4*)&lds_v[st][v_off(d, 4 * sb + 2 * c2 + hf)]);
+          const char* a = sv + (32 * sb + 16 * c2) * kVRow + db * 64;
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a);
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a + 4 * kVRow));
+          const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
             o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 va, __builtin_bit_cast(bf16x8, pk[qb][sb][c2]), o[qb][db], 0, 0, 0);
         }
-    }
-
-    if (t + 1 < ntiles) store_tile(st ^ 1);
-    __syncthreads();
-  }
+  };
+  if (nfull == 0)
+    issue(tr.k_begin, 0, std::true_type{});
+  else
+    issue(tr.k_begin, 0, std::false_type{});
+  for (int64_t t = 0; t < nfull; ++t) tile_step(t, std::false_type{});
+  if (ntiles > nfull) tile_step(nfull, std::true_type{});
 
   // ---- normalise and store O (bf16, RNE)
   uint16_t* __restrict__ og = (uint16_t*)p.o;
@@ -370,8 +413,9 @@ __global__ void __launch_bounds__(kThreads, 2) flash_bf16_kernel(FlashParams p) 
   for (int qb = 0; qb < 2; ++qb) {
     const float l = lsum[qb] + __shfl_xor(lsum[qb], 32);
     const float inv = 1.f / l;
-    if (qvalid[qb]) {
-      uint16_t* dst = og + ((size_t)qrow[qb] * H + head) * 64;
+    const int64_t row = tr.q_begin + wave * kQPerWave + qb * 32 + l32;
+    if (row < tr.q_end) {
+      uint16_t* dst = og + ((size_t)row * H + head) * 64;
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
