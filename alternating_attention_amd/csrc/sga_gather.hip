@@ -3,17 +3,19 @@
 // summary section 3, step two: uniform grid sampling of K/V on the patch
 // grid, and one global mean vector standing for every dropped column).
 //
-// sga_gather_kernel reads K and V once, row by row, and
-//  - writes keep_mask[t] and, for kept tokens, keep_idx[rank] = t;
-//  - copies each kept row of K and V to its compacted slot Kc/Vc[rank];
-//  - sums each dropped row into per-thread fp32 partials, which the block
-//    combines in a fixed order into partials[block] (no float atomics).
-// The kept rank comes from the closed form of the strided lattice: kept
-// patch (r, c) of frame f has rank f*kpf + ((r-oh)/sh)*nw + (c-ow)/sw and
-// special token u has rank f*kpf + nh*nw + (u - gh*gw).
+// sga_gather_kernel reads K and V once, row by row.  Each block owns a
+// contiguous token range:
+//  1. one thread per token evaluates the closed-form selection -- kept patch
+//     (r, c) of frame f has rank f*kpf + ((r-oh)/sh)*nw + (c-ow)/sw, special
+//     token u has rank f*kpf + nh*nw + (u - gh*gw) -- writes keep_mask[t]
+//     and keep_idx[rank] = t, and leaves the rank (or -1) in LDS;
+//  2. all threads stream the rows as 16-byte chunks (fully coalesced): kept
+//     rows are copied to Kc/Vc[rank], dropped rows are summed into per-thread
+//     fp32 partials, combined in a fixed order into partials[block] (no
+//     float atomics).
 // sga_reduce_kernel sums the block partials in a fixed order and divides by
-// |D|, giving kmean and vmean [H, 64] in fp32.  Both kernels are HBM-bound
-// streaming passes; rows are read as 16-byte chunks, fully coalesced.
+// |D|, giving kmean and vmean [H, 64] in fp32.  Both are HBM-bound streaming
+// passes.
 #include "vga_internal.h"
 
 namespace vga {
@@ -23,27 +25,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGatherThreads = 256;
-constexpr int kUnroll = 8;        // tokens in flight per thread
-constexpr int kMaxSlots = 4;      // chunks per thread when a row pair > 256 chunks
+constexpr int kUnroll = 8;          // tokens in flight per thread
+constexpr int kMaxTokensPerBlock = 2048;
 
-struct Rank {
-  bool kept;
-  int64_t rank;
-};
-
-__device__ __forceinline__ Rank sga_rank(const SgaGrid& g, int64_t t) {
-  const int64_t f = t / g.L;
-  const int32_t u = (int32_t)(t - f * g.L);
-  Rank r;
-  if (u >= g.gh * g.gw) {
-    r.kept = true;
-    r.rank = f * g.kpf + (int64_t)g.nh * g.nw + (u - g.gh * g.gw);
-    return r;
-  }
+// Rank of token t among the kept tokens, or -1 when it is dropped.
+__device__ __forceinline__ int32_t sga_rank(const SgaGrid& g, int32_t t) {
+  const int32_t f = t / g.L;
+  const int32_t u = t - f * g.L;
+  const int32_t patches = g.gh * g.gw;
+  if (u >= patches) return f * g.kpf + g.nh * g.nw + (u - patches);
   const int32_t row = u / g.gw, col = u - row * g.gw;
-  r.kept = (row % g.sh == g.oh) && (col % g.sw == g.ow);
-  r.rank = f * g.kpf + (int64_t)((row - g.oh) / g.sh) * g.nw + (col - g.ow) / g.sw;
-  return r;
+  if (row % g.sh != g.oh || col % g.sw != g.ow) return -1;
+  return f * g.kpf + ((row - g.oh) / g.sh) * g.nw + (col - g.ow) / g.sw;
 }
 
 // Accumulate a 16-byte chunk (8 bf16 or 4 fp32) into acc[0..8).
@@ -64,82 +57,80 @@ __device__ __forceinline__ void add_chunk(float* acc, const u32x4& w) {
 template <bool BF16>
 __global__ void __launch_bounds__(kGatherThreads) sga_gather_kernel(GatherParams p) {
   constexpr int kEpc = BF16 ? 8 : 4;          // elements per 16-byte chunk
+  __shared__ int32_t rank_of[kMaxTokensPerBlock];
+  extern __shared__ float red[];              // [G][P][kEpc] when G > 1
+
   const int C = p.H * 64;                     // elements per row
   const int W = C / kEpc;                     // chunks per row
   const int P = 2 * W;                        // chunk slots per token (K, V)
   const int G = P >= kGatherThreads ? 1 : kGatherThreads / P;  // tokens / step
   const int NS = (G * P + kGatherThreads - 1) / kGatherThreads; // slots/thread
-  const int64_t tpb = (p.T + p.blocks - 1) / p.blocks;
-  const int64_t t_begin = (int64_t)blockIdx.x * tpb;
-  const int64_t t_end = min(t_begin + tpb, p.T);
+  const int32_t T = (int32_t)p.T;
+  const int32_t tpb = (T + p.blocks - 1) / p.blocks;
+  const int32_t t_begin = blockIdx.x * tpb;
+  const int32_t t_end = min(t_begin + tpb, T);
 
+  // 1. selection of this block's tokens
+  for (int32_t t = t_begin + threadIdx.x; t < t_end; t += kGatherThreads) {
+    const int32_t r = sga_rank(p.grid, t);
+    rank_of[t - t_begin] = r;
+    p.keep_mask[t] = (uint8_t)(r >= 0);
+    if (r >= 0) p.keep_idx[r] = t;
+  }
+  __syncthreads();
+
+  // 2. stream the rows: chunk slot vt = threadIdx.x + 256*i covers token
+  //    group vt / P and chunk vt % P (K chunks first, then V chunks)
   const u32x4* kg = (const u32x4*)p.k;
   const u32x4* vg = (const u32x4*)p.v;
   u32x4* kc = (u32x4*)p.kc;
   u32x4* vc = (u32x4*)p.vc;
-
-  float acc[kMaxSlots][8];
-  int grp[kMaxSlots], slot[kMaxSlots];
-  bool active[kMaxSlots];
-#pragma unroll
-  for (int i = 0; i < kMaxSlots; ++i) {
-    const int vt = threadIdx.x + kGatherThreads * i;
-    active[i] = i < NS && vt < G * P;
-    grp[i] = vt / P;
-    slot[i] = vt - grp[i] * P;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
-  }
-
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += (int64_t)G * kUnroll) {
-#pragma unroll
-    for (int i = 0; i < kMaxSlots; ++i) {
-      if (!active[i]) continue;
-      const bool is_v = slot[i] >= W;
-      const int ch = is_v ? slot[i] - W : slot[i];
-      const u32x4* src = is_v ? vg : kg;
-      u32x4 w[kUnroll];
-      int64_t tok[kUnroll];
-#pragma unroll
-      for (int uu = 0; uu < kUnroll; ++uu) {
-        tok[uu] = t0 + (int64_t)G * uu + grp[i];
-        if (tok[uu] < t_end) w[uu] = src[tok[uu] * W + ch];
-      }
-#pragma unroll
-      for (int uu = 0; uu < kUnroll; ++uu) {
-        if (tok[uu] >= t_end) continue;
-        const Rank r = sga_rank(p.grid, tok[uu]);
-        if (r.kept) {
-          (is_v ? vc : kc)[r.rank * W + ch] = w[uu];
-        } else {
-          add_chunk<BF16>(acc[i], w[uu]);
-        }
-        if (slot[i] == 0) {
-          p.keep_mask[tok[uu]] = (uint8_t)r.kept;
-          if (r.kept) p.keep_idx[r.rank] = (int32_t)tok[uu];
-        }
-      }
-    }
-  }
-
-  // Block partial: [2][C] = sum over the G token groups, in group order.
   float* out = p.partials + (size_t)blockIdx.x * 2 * C;
-  if (G == 1) {
+  for (int i = 0; i < NS; ++i) {
+    const int vt = threadIdx.x + kGatherThreads * i;
+    if (vt >= G * P) break;
+    const int grp = vt / P, slot = vt - (vt / P) * P;
+    const bool is_v = slot >= W;
+    const int ch = is_v ? slot - W : slot;
+    const u32x4* src = (is_v ? vg : kg) + ch;
+    u32x4* dst = (is_v ? vc : kc) + ch;
+    float acc[8];
 #pragma unroll
-    for (int i = 0; i < kMaxSlots; ++i) {
-      if (!active[i]) continue;
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    int32_t tok = t_begin + grp;
+    // full groups of kUnroll tokens: all loads in flight before any use
+    for (; tok + G * (kUnroll - 1) < t_end; tok += G * kUnroll) {
+      u32x4 w[kUnroll];
 #pragma unroll
-      for (int e = 0; e < kEpc; ++e) out[slot[i] * kEpc + e] = acc[i][e];
+      for (int uu = 0; uu < kUnroll; ++uu) w[uu] = src[(size_t)(tok + G * uu) * W];
+#pragma unroll
+      for (int uu = 0; uu < kUnroll; ++uu) {
+        const int32_t r = rank_of[tok + G * uu - t_begin];
+        if (r >= 0)
+          dst[(size_t)r * W] = w[uu];
+        else
+          add_chunk<BF16>(acc, w[uu]);
+      }
     }
-    return;
-  }
-  extern __shared__ float red[];  // [G][P][kEpc]
+    for (; tok < t_end; tok += G) {
+      const u32x4 w = src[(size_t)tok * W];
+      const int32_t r = rank_of[tok - t_begin];
+      if (r >= 0)
+        dst[(size_t)r * W] = w;
+      else
+        add_chunk<BF16>(acc, w);
+    }
+    if (G == 1) {
 #pragma unroll
-  for (int i = 0; i < kMaxSlots; ++i) {
-    if (!active[i]) continue;
+      for (int e = 0; e < kEpc; ++e) out[slot * kEpc + e] = acc[e];
+    } else {
 #pragma unroll
-    for (int e = 0; e < kEpc; ++e) red[((size_t)grp[i] * P + slot[i]) * kEpc + e] = acc[i][e];
+      for (int e = 0; e < kEpc; ++e) red[((size_t)grp * P + slot) * kEpc + e] = acc[e];
+    }
   }
+  if (G == 1) return;
+
+  // block partial [2][C]: sum over the G token groups in group order
   __syncthreads();
   for (int c = threadIdx.x; c < P * kEpc; c += kGatherThreads) {
     float s = 0.f;
@@ -148,37 +139,64 @@ __global__ void __launch_bounds__(kGatherThreads) sga_gather_kernel(GatherParams
   }
 }
 
-constexpr int kReduceCols = 64;
-constexpr int kReduceGroups = 4;
+// Fixed-order reduction of the block partials: thread (quad q, group g)
+// sums 4 adjacent columns over blocks b = g, g + 16, ...; the 16 group sums
+// are then added pairwise in a fixed tree.
+constexpr int kReduceQuads = 64;
+constexpr int kReduceGroups = 16;
 
-__global__ void __launch_bounds__(kReduceCols * kReduceGroups) sga_reduce_kernel(GatherParams p) {
+__global__ void __launch_bounds__(kReduceQuads * kReduceGroups) sga_reduce_kernel(GatherParams p) {
+  __shared__ f32x4 part[kReduceGroups][kReduceQuads];
   const int C = p.H * 64;
-  const int col = blockIdx.x * kReduceCols + (threadIdx.x % kReduceCols);
-  const int grp = threadIdx.x / kReduceCols;
-  __shared__ float part[kReduceGroups][kReduceCols];
-  float s = 0.f;
-  if (col < 2 * C)
-    for (int b = grp; b < p.blocks; b += kReduceGroups)
-      s += p.partials[(size_t)b * 2 * C + col];
-  part[grp][threadIdx.x % kReduceCols] = s;
+  const int nq = 2 * C / 4;
+  const int qd = threadIdx.x % kReduceQuads;
+  const int g = threadIdx.x / kReduceQuads;
+  const int quad = blockIdx.x * kReduceQuads + qd;
+  f32x4 s = 0.f;
+  if (quad < nq) {
+    const f32x4* src = (const f32x4*)p.partials + quad;
+    int b = g;
+    for (; b + 3 * kReduceGroups < p.blocks; b += 4 * kReduceGroups) {
+      const f32x4 a0 = src[(size_t)b * nq];
+      const f32x4 a1 = src[(size_t)(b + kReduceGroups) * nq];
+      const f32x4 a2 = src[(size_t)(b + 2 * kReduceGroups) * nq];
+      const f32x4 a3 = src[(size_t)(b + 3 * kReduceGroups) * nq];
+      s += a0;
+      s += a1;
+      s += a2;
+      s += a3;
+    }
+    for (; b < p.blocks; b += kReduceGroups) s += src[(size_t)b * nq];
+  }
+  part[g][qd] = s;
   __syncthreads();
-  if (grp == 0 && col < 2 * C) {
-    const int c = threadIdx.x;
-    const float total = (part[0][c] + part[1][c]) + (part[2][c] + part[3][c]);
-    const float mean = p.num_dropped > 0 ? total / (float)p.num_dropped : 0.f;
-    if (col < C)
-      p.kmean[col] = mean;
-    else
-      p.vmean[col - C] = mean;
+  for (int w = kReduceGroups / 2; w >= 1; w /= 2) {
+    if (g < w) part[g][qd] += part[g + w][qd];
+    __syncthreads();
+  }
+  if (g == 0 && quad < nq) {
+    const f32x4 total = part[0][qd];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int col = 4 * quad + e;
+      const float mean = p.num_dropped > 0 ? total[e] / (float)p.num_dropped : 0.f;
+      if (col < C)
+        p.kmean[col] = mean;
+      else
+        p.vmean[col - C] = mean;
+    }
   }
 }
 
 }  // namespace
 
 int32_t gather_blocks(int64_t T) {
+  // enough blocks to fill the chip, few enough that each block's token
+  // ranks fit in LDS
   int64_t b = (T + 127) / 128;
   if (b < 1) b = 1;
   if (b > 1024) b = 1024;
+  while ((T + b - 1) / b > kMaxTokensPerBlock) b *= 2;
   return (int32_t)b;
 }
 
@@ -195,8 +213,9 @@ hipError_t launch_sga_gather(bool bf16, const GatherParams& p, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int rblocks = (2 * C + kReduceCols - 1) / kReduceCols;
-  hipLaunchKernelGGL(sga_reduce_kernel, dim3(rblocks), dim3(kReduceCols * kReduceGroups), 0, s, p);
+  const int nq = 2 * C / 4;
+  const int rblocks = (nq + kReduceQuads - 1) / kReduceQuads;
+  hipLaunchKernelGGL(sga_reduce_kernel, dim3(rblocks), dim3(kReduceQuads * kReduceGroups), 0, s, p);
   return hipGetLastError();
 }
 
