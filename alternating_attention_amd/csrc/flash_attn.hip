@@ -80,10 +80,21 @@ struct TileRange {
   int32_t head;
 };
 
+// Workgroups are dispatched round-robin over the 8 XCDs (block b runs on
+// XCD b % 8), each with its own L2.  Logical tile order gives every XCD one
+// contiguous range, so the query tiles that share a frame's or a head's K/V
+// run on the same XCD at about the same time.
+__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t nblocks) {
+  constexpr int64_t kXcds = 8;
+  const int64_t q = nblocks / kXcds, r = nblocks % kXcds;
+  const int64_t x = b % kXcds;
+  return x * q + min(x, r) + b / kXcds;
+}
+
 template <KeyRange KR>
 __device__ __forceinline__ TileRange tile_range(const FlashParams& p) {
   TileRange t;
-  const int64_t b = blockIdx.x;
+  const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
   if constexpr (KR == KeyRange::kFrame) {
     const int64_t qtpf = (p.L + kBQ - 1) / kBQ;
     const int64_t per_head = qtpf * p.num_frames;

@@ -116,6 +116,24 @@ def cpu_baseline(workload, frames, sga_list, modes, qkv_host, rows_count, seed=7
             "seconds_per_step": step_s}
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE/WRITE_SIZE scaled by a plain copy), or None when the
+    kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_n100.json")
+    src = os.path.join(ROOT, "alternating_attention_amd", "csrc", "flash_attn.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256", {}).get("flash_attn.hip") != sha:
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return k["hbm_bytes"] if k else None
+
+
 def host_bits(t, torch):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
@@ -261,8 +279,9 @@ def run(args):
     ach = flop_dom / (per[dominant]["ms_per_call"] * 1e-3) / 1e12
     kernel = {"global": "flash_bf16_kernel<kGlobal>", "sga": "flash_bf16_kernel<kSga>"}[dominant]
     roofline = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": ach / PEAK_BF16_TFLOPS, "traffic": None, "kernel": kernel,
-                "algorithmic_flops_per_launch": flop_dom}
+                "frac": ach / PEAK_BF16_TFLOPS,
+                "traffic": measured_traffic(kernel) if args.workload == "n100" else None,
+                "kernel": kernel, "algorithmic_flops_per_launch": flop_dom}
 
     result = {
         "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,

@@ -1,0 +1,45 @@
+"""The benchmark's work model against the sizes the pages print
+(tests/golden/page_numbers.json, each entry cited there)."""
+import json
+import os
+
+import bench
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_numbers.json")))
+
+
+def test_attention_matrix_size():
+    g = GOLD["attention_matrix_100_frames"]
+    tokens = g["frames"] * g["tokens_per_frame"]
+    assert tokens == g["total_tokens"]
+    entries, fp16_bytes = bench.attention_matrix(tokens, 2)
+    _, fp32_bytes = bench.attention_matrix(tokens, 4)
+    assert abs(entries - g["entries"]) / g["entries"] < 0.005      # printed to 3 digits
+    assert round(fp16_bytes / 1e9) == g["fp16_gigabytes"]
+    assert round(fp32_bytes / 1e9) == g["fp32_gigabytes"]
+
+
+def test_worked_example_patch_count():
+    g = GOLD["worked_example_patches"]
+    side = g["image_side"] // g["patch_side"]
+    assert side * side == g["patches_per_frame"]
+    assert g["frames"] * side * side == g["total_patches"]
+
+
+def test_flop_model_consistency():
+    # frame attention is global attention restricted to N diagonal blocks
+    N, L, H = 100, 1374, 16
+    assert bench.flops_frame(N, L, H) * N == bench.flops_global(N * L, H)
+    # SGA with every token kept costs exactly global attention
+    assert bench.flops_sga(N * L, N * L, H) == bench.flops_global(N * L, H)
+    # gather reads K and V once and writes the kept rows of both (bf16)
+    assert bench.bytes_gather(10, 4, 2) == 2 * 10 * 2 * 64 * 2 + 2 * 4 * 2 * 64 * 2
+
+
+def test_sga_window_reduces_keys_by_stride_area():
+    g = GOLD["sga_window"]
+    # on a grid divisible by the stride, one kept patch per s x s window
+    from tests.oracle_pins import kept_per_frame_closed_form
+    gh = gw = 8
+    assert kept_per_frame_closed_form(gh, gw, 0, g["stride"], g["stride"], 0, 0) * g["stride"] ** 2 \
+        == gh * gw * g["kept_per_full_window"]
