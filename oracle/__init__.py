@@ -20,6 +20,9 @@ What is computed follows the pages:
   rest run Subsampled Global Attention (all queries kept; K/V on a strided
   patch grid; the diagonal kept; dropped columns replaced by one global mean;
   one shared softmax over the three parts).
+* "VGGT-Omega" notes, section 2 (Register Attention) and architecture section
+  2.3: in a register-attention layer only the per-frame register and camera
+  tokens exchange information across frames; image tokens stay in their frame.
 """
 from __future__ import annotations
 
@@ -33,7 +36,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "vga_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libvga_oracle.so")
 
-MODE_FRAME, MODE_GLOBAL, MODE_SGA = 0, 1, 2
+MODE_FRAME, MODE_GLOBAL, MODE_SGA, MODE_REGISTER = 0, 1, 2, 3
 _F32, _BF16 = 0, 1
 
 
@@ -68,6 +71,8 @@ def _load():
                                    + [vp, i64, vp, i32])
     lib.vgao_schedule.restype = ctypes.c_int
     lib.vgao_schedule.argtypes = [i32, i32, i32, vp]
+    lib.vgao_schedule_register.restype = ctypes.c_int
+    lib.vgao_schedule_register.argtypes = [i32, i32, i32, i32, vp]
     lib.vgao_max_threads.restype = i32
     lib.vgao_max_threads.argtypes = []
     _lib = lib
@@ -112,10 +117,12 @@ def dropped_mean(k, v, N, L, gh, gw, sh, sw, oh, ow):
 
 
 def attention(mode, q, k, v, N, L, gh, gw, scale, sga=None, rows=None, threads=0):
-    """fp64 attention output [len(rows) or T, H, d] for mode FRAME/GLOBAL/SGA.
+    """fp64 attention output [len(rows) or T, H, d] for mode
+    FRAME/GLOBAL/SGA/REGISTER.
 
     q, k, v: [T, H, d] float32, or bf16 given as uint16 bits.
-    sga: dict(stride_h, stride_w, phase_h, phase_w, diagonal, mean_fill)."""
+    sga: dict(stride_h, stride_w, phase_h, phase_w, diagonal, mean_fill);
+    mean_fill 1 is count-weighted, 2 unit-weight."""
     lib = _load()
     qq, dt = _elements(q)
     kk, dtk = _elements(k)
@@ -149,6 +156,17 @@ def schedule(num_global, num_early, use_sga):
     out = np.empty(max(num_global, 0), dtype=np.int32)
     if lib.vgao_schedule(num_global, num_early, int(bool(use_sga)), _ptr(out)) != 0:
         raise ValueError("num_early must lie in [0, num_global]")
+    return out
+
+
+def schedule_register(num_global, num_early, register_every, use_sga):
+    """As schedule(), with every register_every-th slot (counted from slot 0,
+    outside the early ones) running MODE_REGISTER."""
+    lib = _load()
+    out = np.empty(max(num_global, 0), dtype=np.int32)
+    if lib.vgao_schedule_register(num_global, num_early, register_every,
+                                  int(bool(use_sga)), _ptr(out)) != 0:
+        raise ValueError("bad schedule arguments")
     return out
 
 

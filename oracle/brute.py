@@ -7,6 +7,10 @@ the mean-fill column and takes a row softmax -- the "one shared softmax"
 reading of "AVGGT: Rethinking Global Attention for Accelerating VGGT",
 technical summary section 3, step two (SGA).
 
+Register attention ("VGGT-Omega" notes, section 2, Register Attention) is
+the same matrix with a mask that lets special tokens see only special
+tokens (of every frame) and patch tokens see only their own frame.
+
 Inputs are float64 arrays [T, H, d].
 """
 from __future__ import annotations
@@ -30,11 +34,13 @@ def _softmax_rows(z):
 
 
 def attention(mode, q, k, v, N, L, gh, gw, scale, sga=None, mean_copies=False):
-    """mode: 'frame' | 'global' | 'sga'.  Returns [T, H, d] float64.
+    """mode: 'frame' | 'global' | 'sga' | 'register'.  Returns [T, H, d]
+    float64.
 
     mean_copies=True realises the count-weighted mean column literally as |D|
     identical (kmean, vmean) columns with no log term, instead of one column
-    with logit + ln|D| -- the two must agree."""
+    with logit + ln|D| -- the two must agree.  sga["mean_fill"] == 2 is the
+    unit-weight column (logit without ln|D|)."""
     T, H, d = q.shape
     assert T == N * L
     z = scale * np.einsum("ihe,jhe->hij", q, k)          # [H, T, T]
@@ -56,12 +62,21 @@ def attention(mode, q, k, v, N, L, gh, gw, scale, sga=None, mean_copies=False):
             kmean = k[~keep].mean(axis=0)                  # [H, d]
             vmean = v[~keep].mean(axis=0)
             zm = scale * np.einsum("ihe,he->hi", q, kmean)  # [H, T]
-            if mean_copies:
+            if s["mean_fill"] == 2:
+                extra_logits = zm[:, :, None]
+                vals.append(vmean[:, None, :])
+            elif mean_copies:
                 extra_logits = np.repeat(zm[:, :, None], nd, axis=2)
                 vals.append(np.repeat(vmean[:, None, :], nd, axis=1))
             else:
                 extra_logits = (zm + np.log(nd))[:, :, None]
                 vals.append(vmean[:, None, :])
+    elif mode == "register":
+        f = np.arange(T) // L
+        special = (np.arange(T) % L) >= gh * gw
+        same_frame = f[:, None] == f[None, :]
+        both_special = special[:, None] & special[None, :]
+        allowed = np.where(special[:, None], both_special, same_frame)
     elif mode != "global":
         raise ValueError(mode)
     z = np.where(allowed[None], z, -np.inf)

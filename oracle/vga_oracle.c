@@ -19,6 +19,10 @@
  *    query, samples K/V on a strided patch grid, keeps each token's diagonal
  *    term, approximates every dropped K/V column by one global mean vector,
  *    and normalises the three parts under one shared softmax.
+ *  - "VGGT-Omega" notes, section 2 (first architectural change, Register
+ *    Attention) and architecture section 2.3: in some global layers the
+ *    cross-frame exchange runs only among the per-frame register and camera
+ *    tokens, while image tokens attend inside their own frame.
  *
  * Readings where the pages leave a step open (all documented in the design
  * notes, and each one a parameter or a single line below):
@@ -31,7 +35,12 @@
  *    the means over ALL dropped tokens of all frames (one vector per head);
  *  - the diagonal column is added only when the query's own token was
  *    dropped, so no column is ever counted twice;
- *  - with |D| == 0 there is no mean column.
+ *  - with |D| == 0 there is no mean column;
+ *  - mean_fill == 2 is the unit-weight alternative: the same column with
+ *    logit scale*<q, kmean> (it stands for one column, not |D|);
+ *  - register attention: a special-token query (camera and registers are the
+ *    special tokens) attends over the special tokens of all frames; a patch
+ *    query attends over its own frame's tokens, as in frame attention.
  *
  * Layout: Q, K, V are [T, H, d] row-major with T = N*L, token t = f*L + u,
  * u < gh*gw a patch at (u / gw, u % gw) and u >= gh*gw a special token.
@@ -45,7 +54,8 @@
 #include <omp.h>
 #endif
 
-enum { ORC_MODE_FRAME = 0, ORC_MODE_GLOBAL = 1, ORC_MODE_SGA = 2 };
+enum { ORC_MODE_FRAME = 0, ORC_MODE_GLOBAL = 1, ORC_MODE_SGA = 2,
+       ORC_MODE_REGISTER = 3 };
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
 
 /* Read element idx of a fp32 or bf16 array exactly into a double. */
@@ -120,9 +130,14 @@ int64_t vgao_dropped_mean(int32_t N, int32_t L, int32_t gh, int32_t gw,
  * mode SGA   : the columns are the kept tokens; plus row i's own token when
  *              `diagonal` is set and that token was dropped; plus, when
  *              `mean_fill` is set and |D| > 0, one column with key kmean,
- *              value vmean and logit scale*<q,kmean> + ln|D|.
- * For every column j: z_j = scale * <q_i, k_j> (+ ln|D| for the mean
- * column); O_i = sum_j exp(z_j - max z) v_j / sum_j exp(z_j - max z).
+ *              value vmean and logit scale*<q,kmean> + ln|D| (mean_fill 1,
+ *              count-weighted) or scale*<q,kmean> (mean_fill 2, unit weight).
+ * mode REGISTER: a special row's columns are the special tokens of every
+ *              frame in ascending token order; a patch row's columns are the
+ *              L tokens of its own frame.
+ * For every column j: z_j = scale * <q_i, k_j> (+ ln|D| for the
+ * count-weighted mean column); O_i = sum_j exp(z_j - max z) v_j /
+ * sum_j exp(z_j - max z).
  *
  * rows: query tokens (NULL => all T rows in order); out: [nrows, H, d].
  * threads <= 0 uses the OpenMP default.  Returns 0, or -1 on bad arguments
@@ -135,8 +150,10 @@ int vgao_attention(int32_t mode, int32_t N, int32_t L, int32_t gh, int32_t gw,
                    double* out, int32_t threads) {
   if (N < 1 || L < 1 || H < 1 || d < 1 || gh < 0 || gw < 0 || gh * gw > L)
     return -1;
-  if (mode != ORC_MODE_FRAME && mode != ORC_MODE_GLOBAL && mode != ORC_MODE_SGA)
+  if (mode != ORC_MODE_FRAME && mode != ORC_MODE_GLOBAL &&
+      mode != ORC_MODE_SGA && mode != ORC_MODE_REGISTER)
     return -1;
+  if (mean_fill < 0 || mean_fill > 2) return -1;
   int64_t T = (int64_t)N * L;
   if (rows == NULL) nrows = T;
 
@@ -186,9 +203,14 @@ int vgao_attention(int32_t mode, int32_t N, int32_t L, int32_t gh, int32_t gw,
       int64_t nc = 0;
       if (mode == ORC_MODE_GLOBAL) {
         for (int64_t j = 0; j < T; ++j) col[nc++] = j;
-      } else if (mode == ORC_MODE_FRAME) {
+      } else if (mode == ORC_MODE_FRAME ||
+                 (mode == ORC_MODE_REGISTER && i % L < gh * gw)) {
         int64_t f0 = (i / L) * L;
         for (int64_t j = f0; j < f0 + L; ++j) col[nc++] = j;
+      } else if (mode == ORC_MODE_REGISTER) {
+        /* a special query: every special token of every frame */
+        for (int64_t j = 0; j < T; ++j)
+          if (j % L >= gh * gw) col[nc++] = j;
       } else {
         for (int64_t n = 0; n < nkeep; ++n) col[nc++] = keep_idx[n];
         if (diagonal && !keep_mask[i]) col[nc++] = i;
@@ -205,7 +227,7 @@ int vgao_attention(int32_t mode, int32_t N, int32_t L, int32_t gh, int32_t gw,
           z[c] = scale * dot;
         } else {
           for (int32_t e = 0; e < d; ++e) dot += qi[e] * kmean[h * d + e];
-          z[c] = scale * dot + log((double)ndrop);
+          z[c] = scale * dot + (mean_fill == 1 ? log((double)ndrop) : 0.0);
         }
       }
 
@@ -244,6 +266,22 @@ int vgao_schedule(int32_t num_global, int32_t num_early, int32_t use_sga,
   for (int32_t g = 0; g < num_global; ++g)
     out[g] = g < num_early ? ORC_MODE_FRAME
                            : (use_sga ? ORC_MODE_SGA : ORC_MODE_GLOBAL);
+  return 0;
+}
+
+/* Schedule with register attention: as vgao_schedule, except that of the
+ * slots not converted to frame attention, every register_every-th slot
+ * counted from slot 0 (g mod register_every == register_every - 1) runs
+ * register attention.  register_every == 0 gives vgao_schedule.
+ * Returns 0, or -1 on bad arguments. */
+int vgao_schedule_register(int32_t num_global, int32_t num_early,
+                           int32_t register_every, int32_t use_sga,
+                           int32_t* out) {
+  if (register_every < 0) return -1;
+  if (vgao_schedule(num_global, num_early, use_sga, out) != 0) return -1;
+  for (int32_t g = num_early; g < num_global; ++g)
+    if (register_every > 0 && g % register_every == register_every - 1)
+      out[g] = ORC_MODE_REGISTER;
   return 0;
 }
 

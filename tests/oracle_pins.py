@@ -8,14 +8,17 @@ with a mistake planted in the C source and requires that some pin fails.
 Pins (none re-types the oracle's formula or re-calls a routine it uses):
 
 * library routine -- torch's scaled_dot_product_attention (fp64, CPU) for
-  global attention, for frame attention as per-frame calls, and for SGA on an
-  explicitly augmented key set with an additive bias;
+  global attention, for frame attention as per-frame calls, for SGA on an
+  explicitly augmented key set with an additive bias (count-weighted and
+  unit-weight mean column), and for register attention on the compacted set
+  of special tokens;
 * closed forms -- zero queries give count-weighted means of the value rows;
   a hand-sized two-key example; logit ratios with one-hot values;
 * invariants -- rows sum to one; frame == global at one frame; frame ==
   block-diagonal global; SGA at stride 1x1 == global; SGA with identical
   dropped keys == global (exact count weighting); diagonal present once;
   permutation equivariance over frames; Jensen bound on the mean column;
+  register attention with no special tokens == frame attention;
 * brute force -- the numpy matrix formulation (oracle/brute.py).
 """
 from __future__ import annotations
@@ -122,15 +125,18 @@ def pin_zero_query_means(orc):
     keep = keep.astype(bool)
     T = N * L
     for diag in (0, 1):
-        for mean in (0, 1):
+        for mean in (0, 1, 2):
             p = dict(SGA22, diagonal=diag, mean_fill=mean)
             o = orc.attention(orc.MODE_SGA, q, k, v, N, L, gh, gw, SCALE, p)
             for i in range(T):
                 cols = v64[keep].sum(axis=0)
                 n = keep.sum()
-                if mean:                       # |D| copies of vmean = sum of dropped
+                if mean == 1:                  # |D| copies of vmean = sum of dropped
                     cols = cols + v64[~keep].sum(axis=0)
                     n = T
+                elif mean == 2:                # one column holding the mean
+                    cols = cols + v64[~keep].mean(axis=0)
+                    n = n + 1
                 if diag and not keep[i]:
                     cols = cols + v64[i]
                     n = n + 1
@@ -167,7 +173,8 @@ def pin_vs_brute(orc):
     for (N, gh, gw, S, H, seed) in [(2, 8, 8, 5, 2, 0), (3, 5, 7, 1, 1, 9)]:
         s, q, k, v = _shape(N, gh, gw, S, H, seed=seed)
         L = s["L"]
-        for mode, name in ((orc.MODE_GLOBAL, "global"), (orc.MODE_FRAME, "frame")):
+        for mode, name in ((orc.MODE_GLOBAL, "global"), (orc.MODE_FRAME, "frame"),
+                           (orc.MODE_REGISTER, "register")):
             o = orc.attention(mode, q, k, v, N, L, gh, gw, SCALE)
             ref = brute.attention(name, _f64(q), _f64(k), _f64(v), N, L, gh, gw, SCALE)
             assert np.max(np.abs(o - ref)) < 1e-12, name
@@ -176,7 +183,8 @@ def pin_vs_brute(orc):
                   dict(stride_h=2, stride_w=3, phase_h=1, phase_w=0,
                        diagonal=0, mean_fill=1),
                   dict(stride_h=3, stride_w=3, phase_h=2, phase_w=1,
-                       diagonal=1, mean_fill=0)):
+                       diagonal=1, mean_fill=0),
+                  dict(SGA22, mean_fill=2)):
             o = orc.attention(orc.MODE_SGA, q, k, v, N, L, gh, gw, SCALE, p)
             ref = brute.attention("sga", _f64(q), _f64(k), _f64(v), N, L, gh, gw,
                                   SCALE, p)
@@ -203,6 +211,30 @@ def pin_sga_vs_sdpa_augmented(orc):
     bias[:, :T][:, keep] = 0.0
     bias[np.arange(T), np.arange(T)] = 0.0
     bias[:, T] = math.log(nd)
+    ref = _sdpa(_f64(q), ka, va, SCALE, bias)
+    o = orc.attention(orc.MODE_SGA, q, k, v, N, L, gh, gw, SCALE, p)
+    assert np.max(np.abs(o - ref)) < 1e-12
+
+
+def pin_sga_unit_weight_vs_sdpa(orc):
+    # unit-weight mean column: the same augmented key set with bias 0 (one
+    # column) instead of ln|D|
+    s, q, k, v = _shape(2, 5, 6, 2, 2, seed=14)
+    N, L, gh, gw = s["N"], s["L"], 5, 6
+    T = N * L
+    p = dict(stride_h=2, stride_w=3, phase_h=0, phase_w=1, diagonal=1, mean_fill=2)
+    keep = np.zeros(T, bool)
+    for f in range(N):
+        for u in range(L):
+            if u >= gh * gw or ((u // gw) % 2 == 0 and (u % gw) % 3 == 1):
+                keep[f * L + u] = True
+    k64, v64 = _f64(k), _f64(v)
+    ka = np.concatenate([k64, k64[~keep].mean(axis=0)[None]], axis=0)
+    va = np.concatenate([v64, v64[~keep].mean(axis=0)[None]], axis=0)
+    bias = np.full((T, T + 1), -np.inf)
+    bias[:, :T][:, keep] = 0.0
+    bias[np.arange(T), np.arange(T)] = 0.0
+    bias[:, T] = 0.0
     ref = _sdpa(_f64(q), ka, va, SCALE, bias)
     o = orc.attention(orc.MODE_SGA, q, k, v, N, L, gh, gw, SCALE, p)
     assert np.max(np.abs(o - ref)) < 1e-12
@@ -298,7 +330,7 @@ def pin_permutation_equivariance(orc):
     perm = np.array([2, 0, 1])
     idx = (perm[:, None] * L + np.arange(L)[None]).reshape(-1)
     for mode, p in ((orc.MODE_GLOBAL, None), (orc.MODE_FRAME, None),
-                    (orc.MODE_SGA, SGA22)):
+                    (orc.MODE_SGA, SGA22), (orc.MODE_REGISTER, None)):
         a = orc.attention(mode, q, k, v, N, L, 4, 4, SCALE, p)
         b = orc.attention(mode, q[idx], k[idx], v[idx], N, L, 4, 4, SCALE, p)
         assert np.max(np.abs(a[idx] - b)) < 1e-12, mode
@@ -309,10 +341,50 @@ def pin_row_subset(orc):
     N, L = s["N"], s["L"]
     rows = np.array([137, 0, 70, 69, 5])
     for mode, p in ((orc.MODE_GLOBAL, None), (orc.MODE_FRAME, None),
-                    (orc.MODE_SGA, SGA22)):
+                    (orc.MODE_SGA, SGA22), (orc.MODE_REGISTER, None)):
         full = orc.attention(mode, q, k, v, N, L, 8, 8, SCALE, p)
         part = orc.attention(mode, q, k, v, N, L, 8, 8, SCALE, p, rows=rows)
         assert np.array_equal(full[rows], part)
+
+
+# ------------------------------------------------------------ register attention
+def pin_register_vs_sdpa(orc):
+    # special rows: SDPA over the special tokens of all frames, gathered into a
+    # compact set; patch rows: SDPA over their own frame
+    for (N, gh, gw, S, H, seed) in [(3, 4, 5, 3, 2, 71), (2, 8, 8, 5, 2, 72)]:
+        s, q, k, v = _shape(N, gh, gw, S, H, seed=seed)
+        L = s["L"]
+        T = N * L
+        o = orc.attention(orc.MODE_REGISTER, q, k, v, N, L, gh, gw, SCALE)
+        sp = np.array([f * L + u for f in range(N) for u in range(gh * gw, L)])
+        ref = _sdpa(_f64(q[sp]), _f64(k[sp]), _f64(v[sp]), SCALE)
+        assert np.max(np.abs(o[sp] - ref)) < 1e-12, "special rows"
+        for f in range(N):
+            sl = slice(f * L, f * L + gh * gw)
+            fr = slice(f * L, (f + 1) * L)
+            ref = _sdpa(_f64(q[sl]), _f64(k[fr]), _f64(v[fr]), SCALE)
+            assert np.max(np.abs(o[sl] - ref)) < 1e-12, "patch rows"
+        assert len(sp) == N * S and T == N * (gh * gw + S)
+
+
+def pin_register_special_cases(orc):
+    # no special tokens: register attention is frame attention
+    s, q, k, v = _shape(3, 3, 4, 0, 2, seed=73)
+    a = orc.attention(orc.MODE_REGISTER, q, k, v, 3, s["L"], 3, 4, SCALE)
+    b = orc.attention(orc.MODE_FRAME, q, k, v, 3, s["L"], 3, 4, SCALE)
+    assert np.max(np.abs(a - b)) < 1e-14
+    # zero queries: a special row is the mean value of every special token, a
+    # patch row the mean value of its frame
+    s, q, k, v = _shape(3, 3, 3, 2, 2, seed=74)
+    N, L = 3, s["L"]
+    q = np.zeros_like(q)
+    v64 = _f64(v)
+    o = orc.attention(orc.MODE_REGISTER, q, k, v, N, L, 3, 3, SCALE)
+    special = (np.arange(N * L) % L) >= 9
+    for i in range(N * L):
+        f = i // L
+        m = v64[special].mean(axis=0) if special[i] else v64[f * L:(f + 1) * L].mean(axis=0)
+        assert np.max(np.abs(o[i] - m)) < 1e-13, i
 
 
 # ------------------------------------------------------------------- selection
@@ -358,6 +430,13 @@ def pin_schedule(orc):
     assert list(s) == [orc.MODE_FRAME] * 2 + [orc.MODE_GLOBAL] * 3
     assert list(orc.schedule(3, 3, True)) == [orc.MODE_FRAME] * 3
     assert list(orc.schedule(0, 0, True)) == []
+    # every 4th slot (a quarter) runs register attention, early slots excepted
+    F, G, S_, R = orc.MODE_FRAME, orc.MODE_GLOBAL, orc.MODE_SGA, orc.MODE_REGISTER
+    assert list(orc.schedule_register(8, 0, 4, False)) == [G, G, G, R, G, G, G, R]
+    r = orc.schedule_register(24, 8, 4, True)
+    assert list(r) == [F] * 8 + [S_, S_, S_, R] * 4
+    assert int((orc.schedule_register(24, 0, 4, False) == R).sum()) == 6
+    assert list(orc.schedule_register(6, 2, 0, True)) == list(orc.schedule(6, 2, True))
 
 
 ALL_PINS = [v for kname, v in sorted(globals().items()) if kname.startswith("pin_")]

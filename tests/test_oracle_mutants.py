@@ -19,7 +19,15 @@ ORACLE_DIR = os.path.join(ROOT, "oracle")
 
 # (name, original text, planted mistake)
 MUTANTS = [
-    ("drop_log_count", "z[c] = scale * dot + log((double)ndrop);", "z[c] = scale * dot;"),
+    ("drop_log_count", "(mean_fill == 1 ? log((double)ndrop) : 0.0)", "0.0"),
+    ("unit_weight_logged", "(mean_fill == 1 ? log((double)ndrop)", "(mean_fill >= 1 ? log((double)ndrop)"),
+    ("register_specials_see_all", "if (j % L >= gh * gw) col[nc++] = j;", "col[nc++] = j;"),
+    ("register_specials_own_frame",
+     "for (int64_t j = 0; j < T; ++j)\n          if (j % L >= gh * gw)",
+     "for (int64_t j = (i / L) * L; j < (i / L) * L + L; ++j)\n          if (j % L >= gh * gw)"),
+    ("register_first_special_as_patch", "(mode == ORC_MODE_REGISTER && i % L < gh * gw)",
+     "(mode == ORC_MODE_REGISTER && i % L <= gh * gw)"),
+    ("register_schedule_phase", "g % register_every == register_every - 1", "g % register_every == 0"),
     ("diag_double_count", "if (diagonal && !keep_mask[i])", "if (diagonal)"),
     ("diag_ignored", "if (diagonal && !keep_mask[i]) col[nc++] = i;", ";"),
     ("no_scale", "z[c] = scale * dot;\n", "z[c] = dot;\n"),
