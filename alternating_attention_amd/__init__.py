@@ -9,10 +9,17 @@ C names without the ``vga_`` prefix:
 * ``global_attn(q, k, v, frames)`` -> vga_global_attn
 * ``sga_attn(q, k, v, frames, sga)`` -> vga_sga_attn (+ workspace)
 * ``sga_workspace_layout(frames, sga)`` -> vga_sga_workspace_layout
+* ``register_attn(q, k, v, frames)`` -> vga_register_attn (+ workspace)
+* ``register_workspace_layout(frames)`` -> vga_register_workspace_layout
+* ``frame_attn_rows / global_attn_rows / sga_attn_rows(q_rows, k, v, frames,
+  row_begin, ...)`` -> the ``vga_*_attn_rows`` row-range calls
 * ``layer_schedule(num_global, num_early, sga)`` -> vga_layer_schedule
+* ``layer_schedule_register(num_global, num_early, register_every, sga)``
+  -> vga_layer_schedule_register
 
 q, k, v: contiguous [N*L, H, 64] tensors (float32 or bfloat16) on one GPU.
-The library must be built (``alternating_attention_amd._build.build()``);
+The library must be built (``python alternating_attention_amd/_build.py`` or
+``__graft_entry__.build()``);
 importing this module without it raises -- there is no fallback path.
 """
 from __future__ import annotations
@@ -29,12 +36,14 @@ STATUS_NAMES = ["VGA_OK", "VGA_ERR_NULL", "VGA_ERR_SHAPE", "VGA_ERR_DTYPE",
                 "VGA_ERR_PARAM", "VGA_ERR_ALIGN", "VGA_ERR_ALIAS",
                 "VGA_ERR_WORKSPACE", "VGA_ERR_UNSUPPORTED", "VGA_ERR_HIP"]
 VGA_F32, VGA_BF16 = 0, 1
-MODE_FRAME, MODE_GLOBAL, MODE_SGA = 0, 1, 2
+MODE_FRAME, MODE_GLOBAL, MODE_SGA, MODE_REGISTER = 0, 1, 2, 3
 
 # every symbol include/vga.h declares
 EXPORTS = ["vga_frame_attn", "vga_global_attn", "vga_sga_workspace_layout",
-           "vga_sga_attn", "vga_layer_schedule", "vga_status_string",
-           "vga_last_error", "vga_abi_version"]
+           "vga_sga_attn", "vga_register_workspace_layout", "vga_register_attn",
+           "vga_layer_schedule", "vga_layer_schedule_register",
+           "vga_frame_attn_rows", "vga_global_attn_rows", "vga_sga_attn_rows",
+           "vga_status_string", "vga_last_error", "vga_abi_version"]
 
 
 class VgaError(RuntimeError):
@@ -69,6 +78,11 @@ class CLayout(ctypes.Structure):
                 ("kept_per_frame", "num_kept", "num_dropped", "partial_blocks")]
 
 
+class CRegLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in ("qs", "ks", "vs", "os", "total")] + \
+               [("num_special_rows", ctypes.c_int64)]
+
+
 @dataclass(frozen=True)
 class Frames:
     """N frames of a gh x gw patch grid plus S special tokens, H heads of 64."""
@@ -97,13 +111,14 @@ class Frames:
 
 @dataclass(frozen=True)
 class Sga:
-    """Subsampled Global Attention parameters (phase -1: (stride-1)//2)."""
+    """Subsampled Global Attention parameters (phase -1: (stride-1)//2;
+    mean_fill 0 off, 1 / True count-weighted, 2 unit weight)."""
     stride_h: int = 2
     stride_w: int = 2
     phase_h: int = -1
     phase_w: int = -1
     diagonal: bool = True
-    mean_fill: bool = True
+    mean_fill: int = 1
 
     def c(self) -> CSga:
         return CSga(self.stride_h, self.stride_w, self.phase_h, self.phase_w,
@@ -113,7 +128,7 @@ class Sga:
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libvga.so is not built (%s); run "
-                          "alternating_attention_amd._build.build()" % LIB_PATH)
+                          "python alternating_attention_amd/_build.py" % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32 = ctypes.c_void_p, ctypes.c_int32
     for name in ("vga_frame_attn", "vga_global_attn"):
@@ -128,6 +143,23 @@ def _load():
                                  vp, vp, ctypes.c_size_t, vp]
     lib.vga_layer_schedule.restype = ctypes.c_int
     lib.vga_layer_schedule.argtypes = [i32, i32, ctypes.POINTER(CSga), ctypes.POINTER(CLayer)]
+    lib.vga_layer_schedule_register.restype = ctypes.c_int
+    lib.vga_layer_schedule_register.argtypes = [i32, i32, i32, ctypes.POINTER(CSga),
+                                                ctypes.POINTER(CLayer)]
+    lib.vga_register_workspace_layout.restype = ctypes.c_int
+    lib.vga_register_workspace_layout.argtypes = [ctypes.POINTER(CFrames),
+                                                  ctypes.POINTER(CRegLayout)]
+    lib.vga_register_attn.restype = ctypes.c_int
+    lib.vga_register_attn.argtypes = [ctypes.POINTER(CFrames), vp, vp, vp, vp, vp,
+                                      ctypes.c_size_t, vp]
+    i64 = ctypes.c_int64
+    for name in ("vga_frame_attn_rows", "vga_global_attn_rows"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.POINTER(CFrames), i64, i64, vp, vp, vp, vp, vp]
+    lib.vga_sga_attn_rows.restype = ctypes.c_int
+    lib.vga_sga_attn_rows.argtypes = [ctypes.POINTER(CFrames), ctypes.POINTER(CSga), i64, i64,
+                                      vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.vga_status_string.restype = ctypes.c_char_p
     lib.vga_status_string.argtypes = [ctypes.c_int]
     lib.vga_last_error.restype = ctypes.c_char_p
@@ -258,12 +290,112 @@ def workspace_views(workspace, frames: Frames, sga: Sga, dtype_code: int = VGA_B
     )
 
 
+def register_workspace_layout(frames: Frames, dtype_code: int = VGA_BF16) -> CRegLayout:
+    cf = frames.c(dtype_code)
+    lay = CRegLayout()
+    _check(lib.vga_register_workspace_layout(ctypes.byref(cf), ctypes.byref(lay)))
+    return lay
+
+
+def register_attn(q, k, v, frames: Frames, out=None, workspace=None):
+    """Register attention: special tokens attend over the special tokens of
+    all frames, patch tokens over their own frame.  Returns (out, workspace)."""
+    import torch
+    out = _prepare(q, k, v, frames, out)
+    code = _dtype_code(q)
+    lay = register_workspace_layout(frames, code)
+    if workspace is None or workspace.numel() < lay.total:
+        workspace = torch.empty(max(int(lay.total), 1), dtype=torch.uint8, device=q.device)
+    cf = frames.c(code)
+    _check(lib.vga_register_attn(ctypes.byref(cf), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                 out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                 _stream(q.device)))
+    return out, workspace
+
+
+def _prepare_rows(q_rows, k, v, frames: Frames, out):
+    import torch
+    for name, t in (("q_rows", q_rows), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError("%s must be a GPU tensor" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        if t.dtype != k.dtype or t.device != k.device:
+            raise ValueError("q_rows, k, v must share dtype and device")
+    expect = (frames.tokens, frames.num_heads, frames.head_dim)
+    if tuple(k.shape) != expect or tuple(v.shape) != expect:
+        raise ValueError("k/v shape must be [N*L, H, D] = %s" % (expect,))
+    if q_rows.dim() != 3 or tuple(q_rows.shape[1:]) != expect[1:]:
+        raise ValueError("q_rows shape must be [R, H, D]")
+    if out is None:
+        out = torch.empty_like(q_rows)
+    elif (out.shape != q_rows.shape or out.dtype != q_rows.dtype or not out.is_contiguous()
+          or out.device != q_rows.device):
+        raise ValueError("out must be a contiguous tensor like q_rows")
+    return out
+
+
+def frame_attn_rows(q_rows, k, v, frames: Frames, row_begin: int, out=None):
+    """Frame attention for query rows [row_begin, row_begin + len(q_rows))
+    (whole frames) against the full K/V."""
+    out = _prepare_rows(q_rows, k, v, frames, out)
+    cf = frames.c(_dtype_code(k))
+    r1 = row_begin + q_rows.shape[0]
+    _check(lib.vga_frame_attn_rows(ctypes.byref(cf), row_begin, r1, q_rows.data_ptr(),
+                                   k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   _stream(k.device)))
+    return out
+
+
+def global_attn_rows(q_rows, k, v, frames: Frames, row_begin: int, out=None):
+    """Exact global attention for query rows [row_begin, row_begin +
+    len(q_rows)) against all N*L keys."""
+    out = _prepare_rows(q_rows, k, v, frames, out)
+    cf = frames.c(_dtype_code(k))
+    r1 = row_begin + q_rows.shape[0]
+    _check(lib.vga_global_attn_rows(ctypes.byref(cf), row_begin, r1, q_rows.data_ptr(),
+                                    k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                    _stream(k.device)))
+    return out
+
+
+def sga_attn_rows(q_rows, k, v, frames: Frames, sga: Sga, row_begin: int, out=None,
+                  workspace=None):
+    """SGA for query rows [row_begin, row_begin + len(q_rows)); selection and
+    mean over all tokens.  Returns (out, workspace)."""
+    import torch
+    out = _prepare_rows(q_rows, k, v, frames, out)
+    code = _dtype_code(k)
+    lay = sga_workspace_layout(frames, sga, code)
+    if workspace is None or workspace.numel() < lay.total:
+        workspace = torch.empty(int(lay.total), dtype=torch.uint8, device=k.device)
+    cf = frames.c(code)
+    cs = sga.c()
+    r1 = row_begin + q_rows.shape[0]
+    _check(lib.vga_sga_attn_rows(ctypes.byref(cf), ctypes.byref(cs), row_begin, r1,
+                                 q_rows.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                 out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                 _stream(k.device)))
+    return out, workspace
+
+
 def layer_schedule(num_global: int, num_early: int, sga: Sga | None):
     """Per-global-slot list of (mode, CSga) of the training-free pipeline."""
     arr = (CLayer * max(num_global, 1))()
     cs = sga.c() if sga is not None else None
     _check(lib.vga_layer_schedule(num_global, num_early,
                                   ctypes.byref(cs) if cs is not None else None, arr))
+    return [(arr[i].mode, arr[i].sga) for i in range(num_global)]
+
+
+def layer_schedule_register(num_global: int, num_early: int, register_every: int,
+                            sga: Sga | None):
+    """As layer_schedule, with every register_every-th slot (outside the early
+    ones) running register attention."""
+    arr = (CLayer * max(num_global, 1))()
+    cs = sga.c() if sga is not None else None
+    _check(lib.vga_layer_schedule_register(num_global, num_early, register_every,
+                                           ctypes.byref(cs) if cs is not None else None, arr))
     return [(arr[i].mode, arr[i].sga) for i in range(num_global)]
 
 
@@ -276,4 +408,6 @@ def attention(mode: int, q, k, v, frames: Frames, sga: Sga | None = None, out=No
         return global_attn(q, k, v, frames, out)
     if mode == MODE_SGA:
         return sga_attn(q, k, v, frames, sga, out, workspace)[0]
+    if mode == MODE_REGISTER:
+        return register_attn(q, k, v, frames, out)[0]
     raise ValueError("unknown mode %r" % mode)

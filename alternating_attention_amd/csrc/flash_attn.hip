@@ -192,7 +192,7 @@ __global__ void __launch_bounds__(kThreads, 2) flash_bf16_kernel(FlashParams p) 
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int64_t row = min(tr.q_begin + wave * kQPerWave + qb * 32 + l32, tr.q_end - 1);
-      const bool diag = p.use_diag && !sga_kept(p.grid, row);
+      const bool diag = p.use_diag && !sga_kept(p.grid, p.row0 + row);
       const uint16_t* qs = qg + ((size_t)row * H + head) * 64 + 8 * hf;
       const uint16_t* ks = kf + ((size_t)row * H + head) * 64 + 8 * hf;
       const float* kms = p.kmean + head * 64 + 8 * hf;
@@ -497,7 +497,7 @@ __global__ void __launch_bounds__(kF32Threads) flash_f32_kernel(FlashParams p) {
   if constexpr (KR == KeyRange::kSga) {
     const float* kf = (const float*)p.k_full;
     const float* vf = (const float*)p.v_full;
-    if (p.use_diag && !sga_kept(p.grid, row)) {
+    if (p.use_diag && !sga_kept(p.grid, p.row0 + row)) {
       const float* kr = kf + ((size_t)row * H + head) * 64;
       float dot = 0.f;
 #pragma unroll

@@ -1,7 +1,7 @@
-// vga_api.cpp -- the C ABI of libvga.so: argument checks, the SGA
-// workspace layout, the layer schedule and the kernel dispatch.  Every check
-// runs before anything is enqueued, so a failing call leaves the stream
-// untouched.
+// vga_api.cpp -- the C ABI of libvga.so: argument checks, the SGA and
+// register-attention workspace layouts, the layer schedules and the kernel
+// dispatch.  Every check runs before anything is enqueued, so a failing call
+// leaves the stream untouched.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -97,8 +97,10 @@ vga_status resolve_sga(const vga_frames* s, const vga_sga* in, vga_sga* out) {
   if (r.phase_w == -1) r.phase_w = (r.stride_w - 1) / 2;
   if (r.phase_h < 0 || r.phase_h >= r.stride_h || r.phase_w < 0 || r.phase_w >= r.stride_w)
     return fail(VGA_ERR_PARAM, "SGA phase (%d,%d) outside [0, stride)", r.phase_h, r.phase_w);
-  if ((r.diagonal != 0 && r.diagonal != 1) || (r.mean_fill != 0 && r.mean_fill != 1))
-    return fail(VGA_ERR_PARAM, "diagonal and mean_fill must be 0 or 1");
+  if (r.diagonal != 0 && r.diagonal != 1)
+    return fail(VGA_ERR_PARAM, "diagonal must be 0 or 1");
+  if (r.mean_fill < 0 || r.mean_fill > 2)
+    return fail(VGA_ERR_PARAM, "mean_fill must be 0, 1 (count-weighted) or 2 (unit weight)");
   *out = r;
   return VGA_OK;
 }
@@ -169,58 +171,81 @@ vga::FlashParams base_params(const vga_frames* s, const Checked& c, const void* 
   return p;
 }
 
-vga_status dense_attn(vga::KeyRange kr, const vga_frames* s, const void* q, const void* k,
-                      const void* v, void* o, void* stream, const char* what) {
-  Checked c;
-  vga_status st = check_shape(s, &c);
-  if (st != VGA_OK) return st;
-  st = check_tensors(c, q, k, v, o);
-  if (st != VGA_OK) return st;
-  const vga::FlashParams p = base_params(s, c, q, k, v, o);
-  hipStream_t hs = (hipStream_t)stream;
-  const hipError_t e = s->dtype == VGA_BF16 ? vga::launch_flash_bf16(kr, p, hs)
-                                            : vga::launch_flash_f32(kr, p, hs);
-  return finish(e, hs, what);
+hipError_t launch_flash(const vga_frames* s, vga::KeyRange kr, const vga::FlashParams& p,
+                        hipStream_t hs) {
+  return s->dtype == VGA_BF16 ? vga::launch_flash_bf16(kr, p, hs)
+                              : vga::launch_flash_f32(kr, p, hs);
 }
 
-}  // namespace
-
-extern "C" {
-
-vga_status vga_frame_attn(const vga_frames* shape, const void* q, const void* k,
-                          const void* v, void* o, void* stream) {
-  return dense_attn(vga::KeyRange::kFrame, shape, q, k, v, o, stream, "vga_frame_attn");
-}
-
-vga_status vga_global_attn(const vga_frames* shape, const void* q, const void* k,
-                           const void* v, void* o, void* stream) {
-  return dense_attn(vga::KeyRange::kGlobal, shape, q, k, v, o, stream, "vga_global_attn");
-}
-
-vga_status vga_sga_workspace_layout(const vga_frames* shape, const vga_sga* sga,
-                                    vga_sga_ws_layout* out) {
-  Checked c;
-  vga_status st = check_shape(shape, &c);
-  if (st != VGA_OK) return st;
-  vga_sga r;
-  st = resolve_sga(shape, sga, &r);
-  if (st != VGA_OK) return st;
-  if (!out) return fail(VGA_ERR_NULL, "layout output is NULL");
-  fill_layout(shape, c, make_grid(shape, r), out);
+// Rows [r0, r1) of the query side: q_rows/o_rows hold those rows, k/v all
+// T rows.  Checks the range, NULLs, alignment and overlaps.
+vga_status check_rows(const vga_frames* s, const Checked& c, int64_t r0, int64_t r1,
+                      bool whole_frames, const void* q, const void* k, const void* v,
+                      const void* o) {
+  if (r0 < 0 || r1 < r0 || r1 > c.T)
+    return fail(VGA_ERR_SHAPE, "row range [%lld, %lld) outside [0, %lld]", (long long)r0,
+                (long long)r1, (long long)c.T);
+  if (whole_frames && (r0 % s->tokens_per_frame || r1 % s->tokens_per_frame))
+    return fail(VGA_ERR_SHAPE, "row range [%lld, %lld) is not whole frames of %d tokens",
+                (long long)r0, (long long)r1, s->tokens_per_frame);
+  if (r1 == r0) return VGA_OK;  // nothing is read or written
+  if (!q || !k || !v || !o) return fail(VGA_ERR_NULL, "q, k, v and o must be non-NULL");
+  const void* ptrs[4] = {q, k, v, o};
+  for (const void* p : ptrs)
+    if ((uintptr_t)p % 16) return fail(VGA_ERR_ALIGN, "tensor %p is not 16-byte aligned", p);
+  const size_t rb = c.bytes / (size_t)c.T * (size_t)(r1 - r0);
+  if (overlaps(o, rb, q, rb) || overlaps(o, rb, k, c.bytes) || overlaps(o, rb, v, c.bytes))
+    return fail(VGA_ERR_ALIAS, "o overlaps q, k or v");
   return VGA_OK;
 }
 
-vga_status vga_sga_attn(const vga_frames* shape, const vga_sga* sga, const void* q,
-                        const void* k, const void* v, void* o, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+size_t row_bytes(const vga_frames* s) {
+  return (size_t)s->num_heads * vga::kHeadDim * elem_size(s->dtype);
+}
+
+vga_status dense_attn(vga::KeyRange kr, const vga_frames* s, int64_t r0, int64_t r1,
+                      bool ranged, const void* q, const void* k, const void* v, void* o,
+                      void* stream, const char* what) {
+  Checked c;
+  vga_status st = check_shape(s, &c);
+  if (st != VGA_OK) return st;
+  if (!ranged) {
+    r0 = 0;
+    r1 = c.T;
+  }
+  st = check_rows(s, c, r0, r1, kr == vga::KeyRange::kFrame, q, k, v, o);
+  if (st != VGA_OK) return st;
+  if (r1 == r0) return VGA_OK;
+  vga::FlashParams p = base_params(s, c, q, k, v, o);
+  p.num_q = r1 - r0;
+  if (kr == vga::KeyRange::kFrame) {
+    // whole frames: the shard is a frame-attention problem of its own
+    p.k = (const char*)k + (size_t)r0 * row_bytes(s);
+    p.v = (const char*)v + (size_t)r0 * row_bytes(s);
+    p.num_keys = r1 - r0;
+    p.num_frames = (int32_t)((r1 - r0) / s->tokens_per_frame);
+  }
+  hipStream_t hs = (hipStream_t)stream;
+  return finish(launch_flash(s, kr, p, hs), hs, what);
+}
+
+// SGA on query rows [r0, r1): selection, gather and mean over all T tokens,
+// then the shared-softmax attention for the rows.
+vga_status sga_run(const vga_frames* shape, const vga_sga* sga, int64_t r0, int64_t r1,
+                   bool ranged, const void* q, const void* k, const void* v, void* o,
+                   void* workspace, size_t workspace_bytes, void* stream, const char* what) {
   Checked c;
   vga_status st = check_shape(shape, &c);
   if (st != VGA_OK) return st;
   vga_sga r;
   st = resolve_sga(shape, sga, &r);
   if (st != VGA_OK) return st;
-  st = check_tensors(c, q, k, v, o);
-  if (st != VGA_OK) return st;
+  if (!ranged) {
+    r0 = 0;
+    r1 = c.T;
+  }
+  st = check_rows(shape, c, r0, r1, false, q, k, v, o);
+  if (st != VGA_OK || r1 == r0) return st;
   const vga::SgaGrid g = make_grid(shape, r);
   vga_sga_ws_layout w;
   fill_layout(shape, c, g, &w);
@@ -229,9 +254,10 @@ vga_status vga_sga_attn(const vga_frames* shape, const vga_sga* sga, const void*
   if (workspace_bytes < w.total)
     return fail(VGA_ERR_WORKSPACE, "workspace holds %zu bytes, needs %llu", workspace_bytes,
                 (unsigned long long)w.total);
-  if (overlaps(o, c.bytes, workspace, w.total))
+  const size_t rb = row_bytes(shape) * (size_t)(r1 - r0);
+  if (overlaps(o, rb, workspace, w.total))
     return fail(VGA_ERR_ALIAS, "o overlaps the workspace");
-  if (overlaps(q, c.bytes, workspace, w.total) || overlaps(k, c.bytes, workspace, w.total) ||
+  if (overlaps(q, rb, workspace, w.total) || overlaps(k, c.bytes, workspace, w.total) ||
       overlaps(v, c.bytes, workspace, w.total))
     return fail(VGA_ERR_ALIAS, "an input overlaps the workspace");
 
@@ -254,29 +280,43 @@ vga_status vga_sga_attn(const vga_frames* shape, const vga_sga* sga, const void*
   gp.num_dropped = w.num_dropped;
   gp.grid = g;
   hipError_t e = vga::launch_sga_gather(shape->dtype == VGA_BF16, gp, hs);
-  if (e != hipSuccess) return finish(e, hs, "vga_sga_attn (gather)");
+  if (e != hipSuccess) return finish(e, hs, what);
 
   vga::FlashParams p = base_params(shape, c, q, ws + w.kc, ws + w.vc, o);
+  p.num_q = r1 - r0;
   p.num_keys = w.num_kept;
-  p.k_full = k;
-  p.v_full = v;
+  p.row0 = r0;
+  p.k_full = (const char*)k + (size_t)r0 * row_bytes(shape);  // row 0 of the shard
+  p.v_full = (const char*)v + (size_t)r0 * row_bytes(shape);
   p.kmean = gp.kmean;
   p.vmean = gp.vmean;
   p.use_diag = r.diagonal;
-  p.use_mean = r.mean_fill && w.num_dropped > 0;
-  p.log_ndrop = w.num_dropped > 0 ? (float)log((double)w.num_dropped) : 0.f;
+  p.use_mean = r.mean_fill != 0 && w.num_dropped > 0;
+  p.log_ndrop = (r.mean_fill == 1 && w.num_dropped > 0) ? (float)log((double)w.num_dropped)
+                                                        : 0.f;
   p.grid = g;
-  e = shape->dtype == VGA_BF16 ? vga::launch_flash_bf16(vga::KeyRange::kSga, p, hs)
-                               : vga::launch_flash_f32(vga::KeyRange::kSga, p, hs);
-  return finish(e, hs, "vga_sga_attn");
+  return finish(launch_flash(shape, vga::KeyRange::kSga, p, hs), hs, what);
 }
 
-vga_status vga_layer_schedule(int32_t num_global_layers, int32_t num_early_to_frame,
-                              const vga_sga* sga, vga_layer* out) {
+void fill_register_layout(const vga_frames* s, vga_register_ws_layout* w) {
+  const int64_t rows = (int64_t)s->num_frames * s->num_special;
+  const uint64_t sect = align256((uint64_t)rows * row_bytes(s));
+  w->qs = 0;
+  w->ks = sect;
+  w->vs = 2 * sect;
+  w->os = 3 * sect;
+  w->total = 4 * sect;
+  w->num_special_rows = rows;
+}
+
+vga_status schedule(int32_t num_global_layers, int32_t num_early_to_frame,
+                    int32_t register_every, const vga_sga* sga, vga_layer* out) {
   if (num_global_layers < 0 || num_early_to_frame < 0 ||
       num_early_to_frame > num_global_layers)
     return fail(VGA_ERR_PARAM, "need 0 <= num_early (%d) <= num_global (%d)",
                 num_early_to_frame, num_global_layers);
+  if (register_every < 0)
+    return fail(VGA_ERR_PARAM, "register_every %d is negative", register_every);
   if (num_global_layers > 0 && !out) return fail(VGA_ERR_NULL, "schedule output is NULL");
   vga_sga r;
   memset(&r, 0, sizeof r);
@@ -289,6 +329,8 @@ vga_status vga_layer_schedule(int32_t num_global_layers, int32_t num_early_to_fr
     memset(&l, 0, sizeof l);
     if (g < num_early_to_frame) {
       l.mode = VGA_MODE_FRAME;
+    } else if (register_every > 0 && g % register_every == register_every - 1) {
+      l.mode = VGA_MODE_REGISTER;
     } else if (sga) {
       l.mode = VGA_MODE_SGA;
       l.sga = r;
@@ -298,6 +340,145 @@ vga_status vga_layer_schedule(int32_t num_global_layers, int32_t num_early_to_fr
     out[g] = l;
   }
   return VGA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+vga_status vga_frame_attn(const vga_frames* shape, const void* q, const void* k,
+                          const void* v, void* o, void* stream) {
+  return dense_attn(vga::KeyRange::kFrame, shape, 0, 0, false, q, k, v, o, stream,
+                    "vga_frame_attn");
+}
+
+vga_status vga_global_attn(const vga_frames* shape, const void* q, const void* k,
+                           const void* v, void* o, void* stream) {
+  return dense_attn(vga::KeyRange::kGlobal, shape, 0, 0, false, q, k, v, o, stream,
+                    "vga_global_attn");
+}
+
+vga_status vga_frame_attn_rows(const vga_frames* shape, int64_t row_begin, int64_t row_end,
+                               const void* q_rows, const void* k, const void* v,
+                               void* o_rows, void* stream) {
+  return dense_attn(vga::KeyRange::kFrame, shape, row_begin, row_end, true, q_rows, k, v,
+                    o_rows, stream, "vga_frame_attn_rows");
+}
+
+vga_status vga_global_attn_rows(const vga_frames* shape, int64_t row_begin, int64_t row_end,
+                                const void* q_rows, const void* k, const void* v,
+                                void* o_rows, void* stream) {
+  return dense_attn(vga::KeyRange::kGlobal, shape, row_begin, row_end, true, q_rows, k, v,
+                    o_rows, stream, "vga_global_attn_rows");
+}
+
+vga_status vga_sga_workspace_layout(const vga_frames* shape, const vga_sga* sga,
+                                    vga_sga_ws_layout* out) {
+  Checked c;
+  vga_status st = check_shape(shape, &c);
+  if (st != VGA_OK) return st;
+  vga_sga r;
+  st = resolve_sga(shape, sga, &r);
+  if (st != VGA_OK) return st;
+  if (!out) return fail(VGA_ERR_NULL, "layout output is NULL");
+  fill_layout(shape, c, make_grid(shape, r), out);
+  return VGA_OK;
+}
+
+vga_status vga_sga_attn(const vga_frames* shape, const vga_sga* sga, const void* q,
+                        const void* k, const void* v, void* o, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return sga_run(shape, sga, 0, 0, false, q, k, v, o, workspace, workspace_bytes, stream,
+                 "vga_sga_attn");
+}
+
+vga_status vga_sga_attn_rows(const vga_frames* shape, const vga_sga* sga, int64_t row_begin,
+                             int64_t row_end, const void* q_rows, const void* k,
+                             const void* v, void* o_rows, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return sga_run(shape, sga, row_begin, row_end, true, q_rows, k, v, o_rows, workspace,
+                 workspace_bytes, stream, "vga_sga_attn_rows");
+}
+
+vga_status vga_register_workspace_layout(const vga_frames* shape,
+                                         vga_register_ws_layout* out) {
+  Checked c;
+  const vga_status st = check_shape(shape, &c);
+  if (st != VGA_OK) return st;
+  if (!out) return fail(VGA_ERR_NULL, "layout output is NULL");
+  fill_register_layout(shape, out);
+  return VGA_OK;
+}
+
+vga_status vga_register_attn(const vga_frames* shape, const void* q, const void* k,
+                             const void* v, void* o, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  Checked c;
+  vga_status st = check_shape(shape, &c);
+  if (st != VGA_OK) return st;
+  st = check_tensors(c, q, k, v, o);
+  if (st != VGA_OK) return st;
+  vga_register_ws_layout w;
+  fill_register_layout(shape, &w);
+  if (w.total > 0) {
+    if (!workspace) return fail(VGA_ERR_WORKSPACE, "workspace is NULL");
+    if ((uintptr_t)workspace % 16)
+      return fail(VGA_ERR_ALIGN, "workspace is not 16-byte aligned");
+    if (workspace_bytes < w.total)
+      return fail(VGA_ERR_WORKSPACE, "workspace holds %zu bytes, needs %llu", workspace_bytes,
+                  (unsigned long long)w.total);
+    if (overlaps(o, c.bytes, workspace, w.total))
+      return fail(VGA_ERR_ALIAS, "o overlaps the workspace");
+    if (overlaps(q, c.bytes, workspace, w.total) || overlaps(k, c.bytes, workspace, w.total) ||
+        overlaps(v, c.bytes, workspace, w.total))
+      return fail(VGA_ERR_ALIAS, "an input overlaps the workspace");
+  }
+  hipStream_t hs = (hipStream_t)stream;
+  // 1. every row as frame attention (patch rows are final)
+  vga::FlashParams p = base_params(shape, c, q, k, v, o);
+  hipError_t e = launch_flash(shape, vga::KeyRange::kFrame, p, hs);
+  if (e != hipSuccess || w.num_special_rows == 0) return finish(e, hs, "vga_register_attn");
+  // 2. the special rows: pack, attend over all special tokens, unpack over O
+  char* ws = (char*)workspace;
+  vga::SpecialRowsParams sp;
+  memset(&sp, 0, sizeof sp);
+  sp.src[0] = q;
+  sp.src[1] = k;
+  sp.src[2] = v;
+  sp.dst[0] = ws + w.qs;
+  sp.dst[1] = ws + w.ks;
+  sp.dst[2] = ws + w.vs;
+  sp.ntensors = 3;
+  sp.row_chunks = (int32_t)(row_bytes(shape) / 16);
+  sp.rows = w.num_special_rows;
+  sp.L = shape->tokens_per_frame;
+  sp.patches = shape->grid_h * shape->grid_w;
+  sp.S = shape->num_special;
+  sp.to_compact = 1;
+  e = vga::launch_special_rows(sp, hs);
+  if (e != hipSuccess) return finish(e, hs, "vga_register_attn (pack)");
+  vga::FlashParams pg = base_params(shape, c, ws + w.qs, ws + w.ks, ws + w.vs, ws + w.os);
+  pg.num_q = w.num_special_rows;
+  pg.num_keys = w.num_special_rows;
+  e = launch_flash(shape, vga::KeyRange::kGlobal, pg, hs);
+  if (e != hipSuccess) return finish(e, hs, "vga_register_attn (special rows)");
+  sp.src[0] = ws + w.os;
+  sp.dst[0] = o;
+  sp.ntensors = 1;
+  sp.to_compact = 0;
+  return finish(vga::launch_special_rows(sp, hs), hs, "vga_register_attn (unpack)");
+}
+
+vga_status vga_layer_schedule(int32_t num_global_layers, int32_t num_early_to_frame,
+                              const vga_sga* sga, vga_layer* out) {
+  return schedule(num_global_layers, num_early_to_frame, 0, sga, out);
+}
+
+vga_status vga_layer_schedule_register(int32_t num_global_layers,
+                                       int32_t num_early_to_frame,
+                                       int32_t register_every, const vga_sga* sga,
+                                       vga_layer* out) {
+  return schedule(num_global_layers, num_early_to_frame, register_every, sga, out);
 }
 
 const char* vga_status_string(vga_status s) {

@@ -42,8 +42,9 @@ struct FlashParams {
   const float* vmean;   // [H, 64]
   int32_t use_diag;
   int32_t use_mean;
-  float log_ndrop;      // ln |D|
+  float log_ndrop;      // ln |D| (count-weighted mean column), else 0
   SgaGrid grid;
+  int64_t row0;         // token index of query row 0 (row-range calls)
 };
 
 struct GatherParams {
@@ -63,10 +64,25 @@ struct GatherParams {
   SgaGrid grid;
 };
 
+// Copy of the special-token rows between [T, H, 64] tensors and compact
+// [N*S, H, 64] ones (register attention).  Compact row j is token
+// (j / S) * L + patches + j % S.  to_compact: src full -> dst compact, else
+// src compact -> dst full.  Up to three tensors per launch.
+struct SpecialRowsParams {
+  const void* src[3];
+  void* dst[3];
+  int32_t ntensors;
+  int32_t row_chunks;   // 16-byte chunks per row (H * 64 * elem / 16)
+  int64_t rows;         // N * S
+  int32_t L, patches, S;
+  int32_t to_compact;
+};
+
 // Launchers (return the HIP status of the launch).
 hipError_t launch_flash_bf16(KeyRange kr, const FlashParams& p, hipStream_t s);
 hipError_t launch_flash_f32(KeyRange kr, const FlashParams& p, hipStream_t s);
 hipError_t launch_sga_gather(bool bf16, const GatherParams& p, hipStream_t s);
+hipError_t launch_special_rows(const SpecialRowsParams& p, hipStream_t s);
 
 // Number of partial-sum blocks of the gather for T tokens.
 int32_t gather_blocks(int64_t T);

@@ -2,7 +2,7 @@
  * vga.h -- C ABI of the alternating-attention library (libvga.so) for
  * AMD Instinct MI355X (gfx950).
  *
- * The operation set follows two pages:
+ * The operation set follows three pages:
  *  - "VGGT CVPR25 Best Paper" notes, section "Alternating-Attention": a
  *    trunk that alternates frame-wise self-attention (each frame's tokens
  *    attend to their own frame) with global self-attention (every token of
@@ -15,6 +15,10 @@
  *    (plus the special tokens), keeps each token's own diagonal term,
  *    replaces all dropped K/V columns by one global mean column, and puts
  *    the three parts under one shared softmax.
+ *  - "VGGT-Omega" notes, section 2 (first architectural change, Register
+ *    Attention) and architecture section 2.3: some global layers restrict
+ *    the cross-frame exchange to the per-frame register and camera tokens
+ *    (the special tokens here); image tokens stay inside their frame.
  *
  * Tensor layout (all calls): Q, K, V and O are contiguous device arrays of
  * shape [T, H, D] with T = N * L tokens, token-major and frame-major: token
@@ -49,7 +53,7 @@
 extern "C" {
 #endif
 
-#define VGA_ABI_VERSION 1
+#define VGA_ABI_VERSION 2
 
 typedef enum {
   VGA_OK = 0,
@@ -89,13 +93,20 @@ typedef struct {
   int32_t phase_h, phase_w;   /* 0..stride-1; -1 selects (stride - 1) / 2    */
   int32_t diagonal;  /* 0/1: add the query's own (k_i, v_i) column iff its
                         token was dropped (never counted twice)             */
-  int32_t mean_fill; /* 0/1: add one column with key kmean and value vmean
-                        (means over all |D| dropped tokens, per head) whose
-                        logit is scale*<q,kmean> + ln|D|, i.e. it weighs as
-                        |D| copies; absent when |D| == 0                     */
+  int32_t mean_fill; /* 0: no mean column.  1 (count-weighted): one column
+                        with key kmean and value vmean (means over all |D|
+                        dropped tokens, per head) whose logit is
+                        scale*<q,kmean> + ln|D|, i.e. it weighs as |D|
+                        copies.  2 (unit weight): the same column with logit
+                        scale*<q,kmean>.  Absent when |D| == 0.            */
 } vga_sga;
 
-typedef enum { VGA_MODE_FRAME = 0, VGA_MODE_GLOBAL = 1, VGA_MODE_SGA = 2 } vga_mode;
+typedef enum {
+  VGA_MODE_FRAME = 0,
+  VGA_MODE_GLOBAL = 1,
+  VGA_MODE_SGA = 2,
+  VGA_MODE_REGISTER = 3
+} vga_mode;
 
 typedef struct {
   int32_t mode;  /* vga_mode                                                 */
@@ -118,6 +129,15 @@ typedef struct {
   int64_t num_dropped;      /* |D| = T - N * kpf                           */
   int64_t partial_blocks;   /* number of partial-sum blocks                */
 } vga_sga_ws_layout;
+
+/* Byte offsets of the register-attention workspace sections (each 256-byte
+ * aligned): the special-token rows of Q, K, V and of the output, compacted
+ * to [N*S, H, 64] in the element type, frame-major then special order. */
+typedef struct {
+  uint64_t qs, ks, vs, os;
+  uint64_t total;           /* bytes the workspace must hold (0 when S == 0) */
+  int64_t num_special_rows; /* N * S                                         */
+} vga_register_ws_layout;
 
 /* Frame attention ("VGGT CVPR25 Best Paper" notes, "Alternating-Attention";
  * AVGGT section 3, step one): for every frame f, head h and token i of f,
@@ -156,6 +176,55 @@ vga_status vga_sga_attn(const vga_frames* shape, const vga_sga* sga, const void*
  * (counts out of range or bad SGA strides/phases/flags). */
 vga_status vga_layer_schedule(int32_t num_global_layers, int32_t num_early_to_frame,
                               const vga_sga* sga, vga_layer* out);
+
+/* Unit-weight mean-fill (vga_sga.mean_fill == 2) is accepted by every SGA
+ * call above and below; it is the ablation of the count weighting, which
+ * the AVGGT notes leave open. */
+
+/* Register attention (VGGT-Omega notes, section 2, Register Attention):
+ * a special-token query i (u >= gh*gw in its frame) attends over the
+ * special tokens of every frame (N*S columns); a patch query attends over
+ * the L tokens of its own frame, exactly as vga_frame_attn.  With S == 0 it
+ * is frame attention.  workspace: device buffer of at least
+ * vga_register_workspace_layout().total bytes (may be NULL when that is 0),
+ * owned by the caller and rewritten by every call. */
+vga_status vga_register_workspace_layout(const vga_frames* shape,
+                                         vga_register_ws_layout* out);
+vga_status vga_register_attn(const vga_frames* shape, const void* q, const void* k,
+                             const void* v, void* o, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Schedule with register attention: as vga_layer_schedule, except that
+ * among the slots g >= num_early_to_frame, those with
+ * g mod register_every == register_every - 1 become VGA_MODE_REGISTER
+ * (register_every = 4 replaces a quarter of the global layers, as in the
+ * VGGT-Omega notes; 0 replaces none).  Errors as vga_layer_schedule, plus
+ * VGA_ERR_PARAM for register_every < 0. */
+vga_status vga_layer_schedule_register(int32_t num_global_layers,
+                                       int32_t num_early_to_frame,
+                                       int32_t register_every, const vga_sga* sga,
+                                       vga_layer* out);
+
+/* Row-range variants: the share of one device when the query rows are
+ * split across devices (each device holds all of K and V and its own rows
+ * of Q and O).  q_rows and o_rows hold rows [row_begin, row_end) of the
+ * full [T, H, 64] Q and O (q_rows[r] is token row_begin + r); k and v are
+ * the full [T, H, 64] tensors.  The result equals the same rows of the
+ * full call.  0 <= row_begin <= row_end <= T; an empty range enqueues
+ * nothing and reads no pointer (they may be NULL; the SGA variant still
+ * validates its parameters).  vga_frame_attn_rows needs whole frames (row_begin and row_end
+ * multiples of L), else VGA_ERR_SHAPE.  The SGA variant selects and
+ * averages over all T tokens (its workspace is the full-call layout). */
+vga_status vga_frame_attn_rows(const vga_frames* shape, int64_t row_begin, int64_t row_end,
+                               const void* q_rows, const void* k, const void* v,
+                               void* o_rows, void* stream);
+vga_status vga_global_attn_rows(const vga_frames* shape, int64_t row_begin, int64_t row_end,
+                                const void* q_rows, const void* k, const void* v,
+                                void* o_rows, void* stream);
+vga_status vga_sga_attn_rows(const vga_frames* shape, const vga_sga* sga, int64_t row_begin,
+                             int64_t row_end, const void* q_rows, const void* k,
+                             const void* v, void* o_rows, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 const char* vga_status_string(vga_status status);
 const char* vga_last_error(void); /* thread-local detail of the last failure */

@@ -3,8 +3,10 @@
 * the library loads and exports every function include/vga.h declares;
 * argument validation rejects bad calls with the documented status before
   anything would be enqueued (fake, never-dereferenced device pointers);
-* the SGA workspace layout reports the closed-form kept counts;
-* the layer schedule.
+* the SGA workspace layout reports the closed-form kept counts, and the
+  register-attention layout the special-row sections;
+* the layer schedules (with and without register attention) match the
+  oracle's.
 """
 import ctypes
 import os
@@ -38,7 +40,7 @@ def test_exports_every_declared_symbol(vga):
 
 
 def test_abi_version_and_strings(vga):
-    assert vga.abi_version() == 1
+    assert vga.abi_version() == 2
     for code, name in enumerate(vga.STATUS_NAMES):
         assert vga.status_string(code) == name
 
@@ -98,12 +100,74 @@ def test_sga_validation(vga):
     assert call(vga.Sga(stride_h=9)) == 4                  # stride > grid
     assert call(vga.Sga(stride_h=2, phase_h=2)) == 4       # phase >= stride
     assert call(vga.Sga(diagonal=2)) == 4
+    assert call(vga.Sga(mean_fill=3)) == 4
+    assert call(vga.Sga(mean_fill=-1)) == 4
     assert call(vga.Sga(), ws=None) == 7
     assert call(vga.Sga(), nbytes=100) == 7
     assert call(vga.Sga(), ws=FAKE + 0x4000008) == 5
     assert call(vga.Sga(), ws=FAKE + 0x3000000 + 256) == 6  # o overlaps workspace
     assert vga.lib.vga_sga_attn(ctypes.byref(cf), None, FAKE, FAKE, FAKE, FAKE, FAKE, 1,
                                 None) == 1
+
+
+def test_rows_validation(vga):
+    f = _frames(vga)                 # T = 138, L = 69
+    cf = f.c(vga.VGA_BF16)
+    Q, K, V, O = FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000
+
+    def glob(r0, r1, q=Q, o=O):
+        return vga.lib.vga_global_attn_rows(ctypes.byref(cf), r0, r1, q, K, V, o, None)
+
+    def frame(r0, r1):
+        return vga.lib.vga_frame_attn_rows(ctypes.byref(cf), r0, r1, Q, K, V, O, None)
+
+    assert glob(-1, 10) == 2
+    assert glob(20, 10) == 2
+    assert glob(0, 139) == 2
+    assert glob(5, 5) == 0                  # empty range: nothing to enqueue
+    assert glob(0, 10, q=None) == 1
+    assert glob(0, 10, o=Q + 16) == 6       # o overlaps the q rows
+    assert glob(0, 10, o=K + 4096) == 6     # o overlaps k
+    assert frame(0, 70) == 2                # not whole frames
+    assert frame(1, 69) == 2
+    assert frame(69, 69) == 0
+    cs = vga.Sga().c()
+    assert vga.lib.vga_sga_attn_rows(ctypes.byref(cf), ctypes.byref(cs), 0, 200, Q, K, V, O,
+                                     FAKE + 0x4000000, 1 << 30, None) == 2
+    assert vga.lib.vga_sga_attn_rows(ctypes.byref(cf), ctypes.byref(cs), 0, 10, Q, K, V, O,
+                                     None, 1 << 30, None) == 7
+    assert vga.lib.vga_sga_attn_rows(ctypes.byref(cf), ctypes.byref(cs), 3, 3, Q, K, V, O,
+                                     FAKE + 0x4000000, 1 << 30, None) == 0
+    # an empty range reads no pointer
+    assert glob(7, 7, q=None, o=None) == 0
+    assert vga.lib.vga_sga_attn_rows(ctypes.byref(cf), ctypes.byref(cs), 3, 3, None, None,
+                                     None, None, None, 0, None) == 0
+    bad = vga.Sga(stride_h=0).c()
+    assert vga.lib.vga_sga_attn_rows(ctypes.byref(cf), ctypes.byref(bad), 3, 3, None, None,
+                                     None, None, None, 0, None) == 4
+
+
+def test_register_layout_and_validation(vga):
+    f = _frames(vga, num_heads=3)
+    lay = vga.register_workspace_layout(f, vga.VGA_BF16)
+    rows = f.num_frames * f.num_special
+    sect = (rows * 3 * 64 * 2 + 255) // 256 * 256
+    assert lay.num_special_rows == rows
+    assert [lay.qs, lay.ks, lay.vs, lay.os, lay.total] == [0, sect, 2 * sect, 3 * sect, 4 * sect]
+    lay32 = vga.register_workspace_layout(f, vga.VGA_F32)
+    assert lay32.total == 4 * ((rows * 3 * 64 * 4 + 255) // 256 * 256)
+    assert vga.register_workspace_layout(_frames(vga, num_special=0)).total == 0
+    cf = f.c(vga.VGA_BF16)
+
+    def call(ws=FAKE + 0x4000000, nbytes=1 << 30, o=FAKE + 0x3000000):
+        return vga.lib.vga_register_attn(ctypes.byref(cf), FAKE, FAKE + 0x1000000,
+                                         FAKE + 0x2000000, o, ws, nbytes, None)
+
+    assert call(ws=None) == 7
+    assert call(nbytes=lay.total - 1) == 7
+    assert call(ws=FAKE + 0x4000004) == 5
+    assert call(o=FAKE + 0x4000000 - 64) == 6   # o runs into the workspace
+    assert vga.lib.vga_register_attn(None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None) == 1
 
 
 @pytest.mark.parametrize("gh,gw,S,sh,sw,oh,ow", [
@@ -153,3 +217,10 @@ def test_schedule_matches_oracle(vga):
     for G, E, use in [(24, 8, True), (12, 0, False), (5, 5, True)]:
         mine = [m for m, _ in vga.layer_schedule(G, E, vga.Sga() if use else None)]
         assert mine == list(oracle.schedule(G, E, use))
+    for G, E, R, use in [(24, 0, 4, False), (24, 8, 4, True), (10, 3, 3, True), (7, 2, 0, False),
+                         (5, 0, 1, True)]:
+        mine = [m for m, _ in vga.layer_schedule_register(G, E, R, vga.Sga() if use else None)]
+        assert mine == list(oracle.schedule_register(G, E, R, use))
+    with pytest.raises(vga.VgaError) as ei:
+        vga.layer_schedule_register(4, 0, -1, None)
+    assert ei.value.status == 4

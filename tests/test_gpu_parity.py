@@ -8,7 +8,9 @@ Bars (from the arithmetic the kernels use):
   1e-5 of the mean absolute dropped value, in absolute terms.
 Small cases compare every output; the full-size workloads (100, 300 and 800
 frames of 37x37+5 tokens, 16 heads) compare seeded sampled rows, which the
-oracle computes one by one.
+oracle computes one by one.  The same bars apply to register attention, the
+unit-weight mean column and the row-range calls (whose rows are also
+compared with the same rows of the full call).
 """
 import sys
 
@@ -80,10 +82,14 @@ def run_and_compare(vga, frames, q, k, v, modes, sga_list=(), rows=None, tag="")
     sel = slice(None) if rows is None else torch.from_numpy(rows).to(q.device)
     for mode in modes:
         say("case %s mode=%s T=%d H=%d" % (tag, mode, frames.tokens, frames.num_heads))
-        fn = vga.frame_attn if mode == "frame" else vga.global_attn
-        out = fn(q, k, v, frames)
+        if mode == "register":
+            out = vga.register_attn(q, k, v, frames)[0]
+        else:
+            fn = vga.frame_attn if mode == "frame" else vga.global_attn
+            out = fn(q, k, v, frames)
         torch.cuda.synchronize()
-        code = oracle.MODE_FRAME if mode == "frame" else oracle.MODE_GLOBAL
+        code = {"frame": oracle.MODE_FRAME, "global": oracle.MODE_GLOBAL,
+                "register": oracle.MODE_REGISTER}[mode]
         ref = oracle.attention(code, qh, kh, vh, N, L, gh, gw, scale, rows=rows)
         check(host(out[sel]), ref, dtype, "%s %s" % (tag, mode))
     for p in sga_list:
@@ -122,9 +128,10 @@ def test_tiny_fp32_all_modes(vga):
     w = vga_inputs.TINY
     frames = vga.Frames(w.num_frames, w.grid_h, w.grid_w, w.num_special, w.num_heads)
     q, k, v = to_dev(tiny_qkv(frames.tokens, w.num_heads, 64, w.seed), torch.float32)
-    run_and_compare(vga, frames, q, k, v, ["frame", "global"],
+    run_and_compare(vga, frames, q, k, v, ["frame", "global", "register"],
                     [vga.Sga(2, 2, 0, 0, True, True), vga.Sga(2, 2, 0, 0, False, True),
-                     vga.Sga(2, 2, 0, 0, True, False), vga.Sga(3, 3, 1, 1, True, True)],
+                     vga.Sga(2, 2, 0, 0, True, False), vga.Sga(3, 3, 1, 1, True, True),
+                     vga.Sga(2, 2, 0, 0, True, 2)],
                     tag="tiny-f32")
 
 
@@ -151,15 +158,17 @@ def test_small_shapes(vga, shape, dt):
     if gh >= 2 and gw >= 2:
         sgas = [vga.Sga(2, 2, 0, 0, True, True), vga.Sga(min(3, gh), min(2, gw), -1, -1, True, True),
                 vga.Sga(gh, gw, 0, 0, True, True)]    # one patch kept per frame
+        sgas.append(vga.Sga(2, 2, 1, 1, True, 2))     # unit-weight mean column
     sgas.append(vga.Sga(1, 1, 0, 0, True, True))      # nothing dropped: no mean column
-    run_and_compare(vga, frames, q, k, v, ["frame", "global"], sgas, tag="%s-%s" % (shape, dt))
+    run_and_compare(vga, frames, q, k, v, ["frame", "global", "register"], sgas,
+                    tag="%s-%s" % (shape, dt))
 
 
 def test_sga_flag_combinations_bf16(vga):
     frames = vga.Frames(3, 9, 8, 2, 2)
     q, k, v = to_dev(tiny_qkv(frames.tokens, 2, 64, seed=7), torch.bfloat16)
     run_and_compare(vga, frames, q, k, v, [],
-                    [vga.Sga(2, 3, 1, 2, d, mfill) for d in (False, True) for mfill in (False, True)],
+                    [vga.Sga(2, 3, 1, 2, d, mfill) for d in (False, True) for mfill in (0, 1, 2)],
                     tag="flags")
 
 
@@ -212,22 +221,25 @@ def _ff(vga, w):
 
 def _rows_with_tail(T, count, seed, L):
     rows = seeded_rows(T, count, seed)
-    extra = np.array([0, 1, L - 1, L, T - 257, T - 256, T - 2, T - 1])
+    # frame edges, query-tile edges, and the first and last special of frames
+    extra = np.array([0, 1, L - 1, L, T - 257, T - 256, T - 2, T - 1, L - 5, 2 * L - 5,
+                      T // 2 // L * L + L - 3])
     return np.unique(np.concatenate([rows, extra[(extra >= 0) & (extra < T)]]))
 
 
 def test_n4_worked_example(vga):
     frames, q, k, v = _ff(vga, vga_inputs.N4)
     rows = _rows_with_tail(frames.tokens, 600, 41, frames.tokens_per_frame)
-    run_and_compare(vga, frames, q, k, v, ["frame", "global"],
-                    [vga.Sga(2, 2, 0, 0), vga.Sga(3, 3, 1, 1)], rows=rows, tag="N=4")
+    run_and_compare(vga, frames, q, k, v, ["frame", "global", "register"],
+                    [vga.Sga(2, 2, 0, 0), vga.Sga(3, 3, 1, 1), vga.Sga(2, 2, 0, 0, True, 2)],
+                    rows=rows, tag="N=4")
 
 
 def test_n100_full_size(vga):
     frames, q, k, v = _ff(vga, vga_inputs.N100)
     rows = _rows_with_tail(frames.tokens, 96, 42, frames.tokens_per_frame)
-    run_and_compare(vga, frames, q, k, v, ["frame", "global"], [vga.Sga(2, 2, 0, 0)],
-                    rows=rows, tag="N=100")
+    run_and_compare(vga, frames, q, k, v, ["frame", "global", "register"],
+                    [vga.Sga(2, 2, 0, 0)], rows=rows, tag="N=100")
 
 
 def test_n300_full_size_sga(vga):
@@ -239,5 +251,80 @@ def test_n300_full_size_sga(vga):
 def test_n800_full_size_frame_sga(vga):
     frames, q, k, v = _ff(vga, vga_inputs.N800)
     rows = _rows_with_tail(frames.tokens, 32, 44, frames.tokens_per_frame)
-    run_and_compare(vga, frames, q, k, v, ["frame"], [vga.Sga(3, 3, 1, 1)], rows=rows,
-                    tag="N=800")
+    run_and_compare(vga, frames, q, k, v, ["frame", "register"], [vga.Sga(3, 3, 1, 1)],
+                    rows=rows, tag="N=800")
+
+
+# ------------------------------------------------------------ row-range calls
+def _range_cases(T, L):
+    # empty, one row, unaligned, tile-straddling, whole frames, everything
+    return [(0, 0), (5, 6), (3, min(T, 70)), (max(0, T - 300), T - 1), (L, min(T, 3 * L)),
+            (0, T)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_rows_small(vga, dt):
+    frames = vga.Frames(5, 11, 13, 4, 2)          # L = 147, T = 735
+    T, L = frames.tokens, frames.tokens_per_frame
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    q, k, v = to_dev(tiny_qkv(T, 2, 64, seed=123), tdt)
+    qh, kh, vh = host(q), host(k), host(v)
+    sga = vga.Sga(2, 3, 1, 0, True, 1)
+    full = {"global": vga.global_attn(q, k, v, frames),
+            "frame": vga.frame_attn(q, k, v, frames),
+            "sga": vga.sga_attn(q, k, v, frames, sga)[0]}
+    for r0, r1 in _range_cases(T, L):
+        rows = np.arange(r0, r1)
+        for mode in ("global", "frame", "sga"):
+            if mode == "frame" and (r0 % L or r1 % L):
+                with pytest.raises(vga.VgaError) as ei:
+                    vga.frame_attn_rows(q[r0:r1].contiguous(), k, v, frames, r0)
+                assert ei.value.status == 2
+                continue
+            say("case rows-%s %s [%d, %d)" % (dt, mode, r0, r1))
+            qr = q[r0:r1].contiguous()
+            if mode == "global":
+                out = vga.global_attn_rows(qr, k, v, frames, r0)
+            elif mode == "frame":
+                out = vga.frame_attn_rows(qr, k, v, frames, r0)
+            else:
+                out = vga.sga_attn_rows(qr, k, v, frames, sga, r0)[0]
+            torch.cuda.synchronize()
+            assert out.shape[0] == r1 - r0
+            if r1 == r0:
+                continue
+            code = {"global": oracle.MODE_GLOBAL, "frame": oracle.MODE_FRAME,
+                    "sga": oracle.MODE_SGA}[mode]
+            ref = oracle.attention(code, qh, kh, vh, frames.num_frames, L, 11, 13, 0.125,
+                                   oracle_sga(sga) if mode == "sga" else None, rows=rows)
+            check(host(out), ref, dt, "rows %s [%d,%d)" % (mode, r0, r1))
+            # the same rows of the full call: identical in fp32 (one lane per
+            # query); in bf16 a shard may take the exact-max path on other tiles
+            a, b = out.float(), full[mode][r0:r1].float()
+            if dt == "f32":
+                assert torch.equal(a, b), mode
+            else:
+                assert float((a - b).abs().max()) <= BF16_MAX
+
+
+def test_rows_n100_one_of_eight(vga):
+    # one device's share when 100 frames are split over 8 devices by query
+    # rows: rows [3T/8, 4T/8) against all 137,400 keys
+    frames, q, k, v = _ff(vga, vga_inputs.N100)
+    T, L = frames.tokens, frames.tokens_per_frame
+    r0, r1 = 3 * T // 8, 4 * T // 8
+    qh, kh, vh = host(q), host(k), host(v)
+    rows = np.unique(np.concatenate([seeded_rows(r1 - r0, 48, 45) + r0,
+                                     [r0, r0 + 1, r1 - 2, r1 - 1]]))
+    say("case rows-N100 global [%d, %d)" % (r0, r1))
+    out = vga.global_attn_rows(q[r0:r1].contiguous(), k, v, frames, r0)
+    torch.cuda.synchronize()
+    ref = oracle.attention(oracle.MODE_GLOBAL, qh, kh, vh, 100, L, 37, 37, 0.125, rows=rows)
+    check(host(out[torch.from_numpy(rows - r0).cuda()]), ref, "bf16", "N=100 rows global")
+    sga = vga.Sga(2, 2, 0, 0)
+    say("case rows-N100 sga [%d, %d)" % (r0, r1))
+    out = vga.sga_attn_rows(q[r0:r1].contiguous(), k, v, frames, sga, r0)[0]
+    torch.cuda.synchronize()
+    ref = oracle.attention(oracle.MODE_SGA, qh, kh, vh, 100, L, 37, 37, 0.125, oracle_sga(sga),
+                           rows=rows)
+    check(host(out[torch.from_numpy(rows - r0).cuda()]), ref, "bf16", "N=100 rows sga")
