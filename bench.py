@@ -7,14 +7,23 @@ layer, one exact global-attention layer and one Subsampled Global Attention
 layer (key selection, gather + mean, attention).  The default workload is
 100 frames x 1374 tokens (37x37 patches + 5 specials), 16 heads x 64, bf16.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload n100|n300|n800]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload n100|n300|n800|n800reg|shard8|sweep]
 
 Prints ONE JSON line.  `value` is tokens/s through one step (T / step time).
 Other workloads:
-  n300 -- one exact global layer vs one SGA 2x2 layer at 300 frames (speedup,
-          output deviation);
-  n800 -- the 24-slot AVGGT schedule (8 frame + 16 SGA 3x3) at 800 frames vs
-          one exact global layer timed once (x24).
+  n300    -- one exact global layer vs one SGA 2x2 layer at 300 frames
+             (speedup, output deviation);
+  n800    -- the 24-slot AVGGT schedule (8 frame + 16 SGA 3x3) at 800 frames
+             vs one exact global layer timed once (x24);
+  n800reg -- register attention vs SGA 3x3 at 800 frames, each against one
+             exact global layer (speed and output deviation), and the 24-slot
+             schedules that use them;
+  shard8  -- one device's share of an 8-way query-row split at 800 frames
+             (rows [3T/8, 4T/8) against all keys), exact global and SGA 3x3,
+             against the full layers;
+  sweep   -- SGA at 300 frames over strides 2x2, 3x3, 4x4 and the ablations
+             (unit-weight mean column, no diagonal, no mean column).
 --copy-probe runs a plain 1 GiB device copy (for scaling HBM counters).
 """
 from __future__ import annotations
@@ -88,17 +97,22 @@ class Timer:
         return [a.elapsed_time(b) for a, b in self.pairs]
 
 
-def cpu_baseline(workload, frames, sga_list, modes, qkv_host, rows_count, seed=7):
+def cpu_baseline(workload, frames, sga_list, modes, qkv_host, rows_count, seed=7,
+                 row_range=None):
     """The fp64 oracle on a bounded sample: `rows_count` seeded query rows
-    (all heads) of each mode of the step, extrapolated x T / rows."""
+    (all heads) of each mode of the step, extrapolated x (rows of the step) /
+    rows_count.  row_range: the step's query rows (default all T)."""
     import oracle
     q, k, v = qkv_host
     T = frames.tokens
-    rows = np.sort(np.random.default_rng(seed).choice(T, size=rows_count, replace=False))
+    r0, r1 = row_range if row_range is not None else (0, T)
+    rows = r0 + np.sort(np.random.default_rng(seed).choice(r1 - r0, size=rows_count,
+                                                            replace=False))
     args = (frames.num_frames, frames.tokens_per_frame, frames.grid_h, frames.grid_w, 0.125)
     t0 = time.perf_counter()
     for mode in modes:
-        code = oracle.MODE_FRAME if mode == "frame" else oracle.MODE_GLOBAL
+        code = {"frame": oracle.MODE_FRAME, "global": oracle.MODE_GLOBAL,
+                "register": oracle.MODE_REGISTER}[mode]
         oracle.attention(code, q, k, v, *args, rows=rows)
     for p in sga_list:
         oracle.attention(oracle.MODE_SGA, q, k, v, *args,
@@ -106,13 +120,14 @@ def cpu_baseline(workload, frames, sga_list, modes, qkv_host, rows_count, seed=7
                               phase_w=p.phase_w, diagonal=int(p.diagonal),
                               mean_fill=int(p.mean_fill)), rows=rows)
     dt = time.perf_counter() - t0
-    step_s = dt * T / rows_count
-    return {"value": T / step_s, "unit": "tokens/s", "cores": oracle.max_threads(),
+    step_s = dt * (r1 - r0) / rows_count
+    return {"value": (r1 - r0) / step_s, "unit": "tokens/s", "cores": oracle.max_threads(),
             "kind": "oracle",
             "sample": "%d seeded query rows x %d heads of each layer of the step (%s), "
-                      "timed %.1f s, extrapolated x T/%d" % (
+                      "timed %.1f s, extrapolated x %d/%d" % (
                           rows_count, frames.num_heads,
-                          "+".join(list(modes) + ["sga"] * len(sga_list)), dt, rows_count),
+                          "+".join(list(modes) + ["sga"] * len(sga_list)), dt, r1 - r0,
+                          rows_count),
             "seconds_per_step": step_s}
 
 
@@ -138,13 +153,27 @@ def host_bits(t, torch):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def deviation(a, b):
+    """max-abs, mean-abs and relative L2 of a - b (b the exact reference)."""
+    d = a.float() - b.float()
+    return {"max_abs": float(d.abs().max()), "mean_abs": float(d.abs().mean()),
+            "rel_l2": float(d.norm() / b.float().norm())}
+
+
+def flops_register(N, L, S, H, d=HEAD_DIM):
+    """Frame attention for every row plus special rows over all N*S specials
+    (the special rows' frame-attention work is included: the kernel does it)."""
+    return flops_frame(N, L, H, d) + 4.0 * (N * S) ** 2 * d * H
+
+
 # ---------------------------------------------------------------- workloads
 def run(args):
     import torch
     import alternating_attention_amd as vga
     import vga_inputs
 
-    w = vga_inputs.WORKLOADS[args.workload]
+    base = {"n800reg": "n800", "shard8": "n800", "sweep": "n300"}
+    w = vga_inputs.WORKLOADS[base.get(args.workload, args.workload)]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     frames = vga.Frames(w.num_frames, w.grid_h, w.grid_w, w.num_special, w.num_heads)
@@ -211,6 +240,66 @@ def run(args):
         work = {"frame": 8 * flops_frame(N, L, H), "sga": 16 * flops_sga(T, nk, H)}
         dominant, modes, sgas = "sga", ["frame"], [sga]
         assert len(plan) == 24
+    elif args.workload == "n800reg":
+        sga = vga.Sga(3, 3, 1, 1, True, True)
+        lay = vga.sga_workspace_layout(frames, sga)
+        ws = torch.empty(int(lay.total), dtype=torch.uint8, device=dev)
+        rlay = vga.register_workspace_layout(frames)
+        rws = torch.empty(int(rlay.total), dtype=torch.uint8, device=dev)
+        nk = int(lay.num_kept)
+        out_c = torch.empty_like(q)
+        desc = ("N=800 frames x 1374 tokens = 1,099,200 tokens, 16 heads x 64, bf16; "
+                "step = one register-attention layer (specials of all frames exchange, "
+                "patches in frame) + one SGA 3x3 layer (phase 1, diagonal, mean-fill); "
+                "exact global layer timed once beside it")
+
+        def step():
+            timed("register", lambda: vga.register_attn(q, k, v, frames, out_c, rws))
+            timed("sga", lambda: vga.sga_attn(q, k, v, frames, sga, out_b, ws))
+        work = {"register": flops_register(N, L, w.num_special, H),
+                "sga": flops_sga(T, nk, H)}
+        dominant, modes, sgas = "sga", ["register"], [sga]
+    elif args.workload == "shard8":
+        sga = vga.Sga(3, 3, 1, 1, True, True)
+        lay = vga.sga_workspace_layout(frames, sga)
+        ws = torch.empty(int(lay.total), dtype=torch.uint8, device=dev)
+        nk = int(lay.num_kept)
+        r0, r1 = 3 * T // 8, 4 * T // 8
+        qr = q[r0:r1].contiguous()
+        o_r = torch.empty_like(qr)
+        desc = ("N=800 frames x 1374 tokens = 1,099,200 tokens, 16 heads x 64, bf16; "
+                "step = one device's share of an 8-way query-row split: rows [%d, %d) "
+                "against all keys, exact global layer + SGA 3x3 layer (selection and mean "
+                "over all tokens); the full layers timed once beside it" % (r0, r1))
+
+        def step():
+            timed("global", lambda: vga.global_attn_rows(qr, k, v, frames, r0, o_r))
+            timed("sga", lambda: vga.sga_attn_rows(qr, k, v, frames, sga, r0, o_r, ws))
+        work = {"global": 4.0 * (r1 - r0) * T * HEAD_DIM * H,
+                "sga": 4.0 * (r1 - r0) * nk * HEAD_DIM * H}
+        dominant, modes, sgas = "global", ["global"], [sga]
+    elif args.workload == "sweep":
+        variants = [("sga_2x2", vga.Sga(2, 2, 0, 0, True, 1)),
+                    ("sga_3x3", vga.Sga(3, 3, 1, 1, True, 1)),
+                    ("sga_4x4", vga.Sga(4, 4, 1, 1, True, 1)),
+                    ("sga_2x2_unit_mean", vga.Sga(2, 2, 0, 0, True, 2)),
+                    ("sga_2x2_no_diag", vga.Sga(2, 2, 0, 0, False, 1)),
+                    ("sga_2x2_no_mean", vga.Sga(2, 2, 0, 0, True, 0))]
+        lays = {n: vga.sga_workspace_layout(frames, p) for n, p in variants}
+        ws = torch.empty(int(max(l.total for l in lays.values())), dtype=torch.uint8,
+                         device=dev)
+        outs = {n: torch.empty_like(q) for n, _ in variants}
+        desc = ("N=300 frames x 1374 tokens = 412,200 tokens, 16 heads x 64, bf16; "
+                "step = SGA at strides 2x2 (phase 0), 3x3 and 4x4 (phase 1), and at 2x2 "
+                "with a unit-weight mean column, without the diagonal, without the mean "
+                "column; exact global layer timed once beside it")
+
+        def step():
+            for n, p in variants:
+                timed(n, lambda p=p, n=n: vga.sga_attn(q, k, v, frames, p, outs[n], ws))
+        work = {n: flops_sga(T, int(lays[n].num_kept), H) for n, _ in variants}
+        dominant, modes, sgas = "sga_2x2", [], [variants[0][1]]
+        sga, nk, lay = variants[0][1], int(lays["sga_2x2"].num_kept), lays["sga_2x2"]
     else:
         raise SystemExit("unknown workload")
 
@@ -249,6 +338,67 @@ def run(args):
         per["sga"]["kept_per_frame"] = int(lay.kept_per_frame)
 
     extra = {}
+    if args.workload == "n800reg":
+        log("exact global layer, timed once")
+        g = Timer(torch)
+        with g:
+            vga.global_attn(q, k, v, frames, out)
+        torch.cuda.synchronize()
+        gms = g.ms()[0]
+        rms, sms = per["register"]["ms_per_call"], per["sga"]["ms_per_call"]
+        fr = Timer(torch)
+        with fr:
+            vga.frame_attn(q, k, v, frames, out_b)
+        torch.cuda.synchronize()
+        fms = fr.ms()[0]
+        per["global_once"] = {"ms_per_call": gms,
+                              "tflops": flops_global(T, H) / (gms * 1e-3) / 1e12}
+        per["frame_once"] = {"ms_per_call": fms}
+        extra["register_vs_exact_layer_speedup"] = gms / rms
+        extra["sga_vs_exact_layer_speedup"] = gms / sms
+        vga.register_attn(q, k, v, frames, out_c, rws)
+        vga.sga_attn(q, k, v, frames, sga, out_b, ws)
+        torch.cuda.synchronize()
+        extra["register_deviation"] = deviation(out_c, out)
+        extra["sga_deviation"] = deviation(out_b, out)
+        # 24 global slots, from the per-layer times above
+        sched = {"exact_24_global": 24 * gms,
+                 "avggt_8frame_16sga": 8 * fms + 16 * sms,
+                 "omega_quarter_register_18global_6register": 18 * gms + 6 * rms,
+                 "avggt_plus_register_8frame_4register_12sga": 8 * fms + 4 * rms + 12 * sms}
+        extra["schedules_ms_from_layer_times"] = sched
+        plan = [m for m, _ in vga.layer_schedule_register(24, 8, 4, sga)]
+        assert plan.count(vga.MODE_REGISTER) == 4 and plan.count(vga.MODE_SGA) == 12
+    if args.workload == "shard8":
+        log("full layers, timed once")
+        g = Timer(torch)
+        with g:
+            vga.global_attn(q, k, v, frames, out)
+        with g:
+            vga.sga_attn(q, k, v, frames, sga, out_b, ws)
+        torch.cuda.synchronize()
+        gms, sfull = g.ms()
+        per["global_full_once"] = {"ms_per_call": gms}
+        per["sga_full_once"] = {"ms_per_call": sfull}
+        extra["row_split_efficiency_global"] = (gms / 8) / per["global"]["ms_per_call"]
+        extra["row_split_efficiency_sga"] = (sfull / 8) / per["sga"]["ms_per_call"]
+        vga.global_attn_rows(qr, k, v, frames, r0, o_r)
+        torch.cuda.synchronize()
+        extra["shard_vs_full_rows"] = deviation(o_r, out[r0:r1])
+    if args.workload == "sweep":
+        log("exact global layer, timed once")
+        g = Timer(torch)
+        with g:
+            vga.global_attn(q, k, v, frames, out)
+        torch.cuda.synchronize()
+        gms = g.ms()[0]
+        per["global_once"] = {"ms_per_call": gms}
+        for n, p in variants:
+            vga.sga_attn(q, k, v, frames, p, outs[n], ws)
+            torch.cuda.synchronize()
+            per[n]["kept_per_frame"] = int(lays[n].kept_per_frame)
+            per[n]["speedup_vs_exact"] = gms / per[n]["ms_per_call"]
+            per[n]["deviation_vs_exact"] = deviation(outs[n], out)
     if args.workload in ("n300", "n800"):
         if args.workload == "n800":
             log("exact global layer, timed once")
@@ -277,7 +427,8 @@ def run(args):
 
     flop_dom = work[dominant] / per[dominant]["calls_per_step"]
     ach = flop_dom / (per[dominant]["ms_per_call"] * 1e-3) / 1e12
-    kernel = {"global": "flash_bf16_kernel<kGlobal>", "sga": "flash_bf16_kernel<kSga>"}[dominant]
+    kernel = {"global": "flash_bf16_kernel<kGlobal>", "sga": "flash_bf16_kernel<kSga>",
+              "sga_2x2": "flash_bf16_kernel<kSga>"}[dominant]
     roofline = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / PEAK_BF16_TFLOPS,
                 "traffic": measured_traffic(kernel) if args.workload == "n100" else None,
@@ -297,7 +448,9 @@ def run(args):
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, %d rows per layer)" % args.cpu_rows)
         qkv = (host_bits(q, torch), host_bits(k, torch), host_bits(v, torch))
-        result["cpu_baseline"] = cpu_baseline(w, frames, sgas, modes, qkv, args.cpu_rows)
+        result["cpu_baseline"] = cpu_baseline(
+            w, frames, sgas, modes, qkv, args.cpu_rows,
+            row_range=(3 * T // 8, 4 * T // 8) if args.workload == "shard8" else None)
     return result
 
 
@@ -319,7 +472,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="n100", choices=["n100", "n300", "n800"])
+    ap.add_argument("--workload", default="n100",
+                    choices=["n100", "n300", "n800", "n800reg", "shard8", "sweep"])
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
@@ -331,7 +485,8 @@ def main():
     if args.copy_probe:
         copy_probe()
         return
-    defaults = {"n100": (10, 2), "n300": (3, 1), "n800": (1, 1)}[args.workload]
+    defaults = {"n100": (10, 2), "n300": (3, 1), "n800": (1, 1), "n800reg": (2, 1),
+                "shard8": (2, 1), "sweep": (2, 1)}[args.workload]
     args.steps = args.steps if args.steps is not None else defaults[0]
     args.warmup = args.warmup if args.warmup is not None else defaults[1]
     res = run(args)
