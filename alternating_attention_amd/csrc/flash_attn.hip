@@ -22,17 +22,28 @@
 // register r of lane half h holds key 16*(r/8) + 8*h + r%8 -- exactly the
 // B-operand k-slot order of the PV product.  V stays in its natural layout;
 // the PV A operand (V^T) comes from ds_read_b64_tr_b16 transposed reads.
-// K/V tiles move global -> LDS with global_load_lds_dwordx4 (no registers),
-// double buffered: tile t+1 loads while tile t is computed.
+// K/V tiles of 64 keys move global -> LDS with global_load_lds_dwordx4 (no
+// registers) through a ring of three stages; a ragged last tile is taken
+// first (softmax sums do not depend on the key order), so every later tile
+// is full and needs no masking.
+//
+// Software pipeline over 32-key sub-tiles j: step j issues the QK^T MFMAs
+// of sub-tile j+1 and the PV MFMAs of sub-tile j-1 while the VALU computes
+// the softmax of sub-tile j; the three are independent, and sched barriers
+// interleave them one MFMA to one pair of scores, so the matrix core and
+// the VALU of one wave run side by side (a second wave per SIMD fills the
+// gaps).  Each tile costs one barrier: tile t+1 must have landed before its
+// first QK, and tile t+2 then loads into the stage of tile t-1, whose last
+// reader (the PV of its second sub-tile) ran before that barrier.
 //
 // Softmax: the MFMA produces exact fp32 dot products of the bf16 rows; one
 // FMA per score turns them into log2 units and subtracts the row's
-// reference max m.  m is updated lazily: the first tile, or a tile whose
-// probabilities sum above 2^16 in a lane, takes a wave-uniform slow path
-// that recomputes S, raises m to the tile max and rescales O and l (the
-// textbook online softmax); every other tile uses P = exp2(S - m) as is.
-// P is rounded to bf16 (RNE) for the PV MFMA; l (summed from the rounded P)
-// and O accumulate in fp32.
+// reference max m.  m is updated lazily: the first sub-tile, or a sub-tile
+// whose probabilities sum above 2^16 in a lane, takes a wave-uniform slow
+// path that (re)computes its scores, raises m to the sub-tile max and
+// rescales O and l (the textbook online softmax); every other sub-tile uses
+// P = exp2(S - m) as is.  P is rounded to bf16 (RNE) for the PV MFMA; l
+// (summed from the rounded P) and O accumulate in fp32.
 //
 // fp32 path: a plain VALU kernel (one lane per query and head, exact online
 // softmax in fp32), used for fp32 inputs.
@@ -136,7 +147,7 @@ constexpr int kKTile = kBK * kKRow, kVTile = kBK * kVRow;     // 9216, 10240
 constexpr int kStage = kKTile + kVTile;                        // 19456
 constexpr int kKInstr = kKTile / 1024, kVInstr = kVTile / 1024;  // 9, 10
 constexpr int kDmaSlots = (kKInstr + kVInstr + 3) / 4;         // per wave: 5
-constexpr int kStages = 2;
+constexpr int kStages = 3;
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -144,7 +155,7 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 template <KeyRange KR>
 __global__ void __launch_bounds__(kThreads, 2) flash_bf16_kernel(FlashParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[kStages * kStage];
+  __shared__ __attribute__((aligned(16))) char lds[kStages][kStage];
 
   const TileRange tr = tile_range<KR>(p);
   const int tid = threadIdx.x;
@@ -268,7 +279,7 @@ __global__ void __launch_bounds__(kThreads, 2) flash_bf16_kernel(FlashParams p) 
   const char* vbytes = (const char*)p.v + (int64_t)head * 128;
   // Issue the DMA of the tile at key0 into `stage`; with clamp (ragged last
   // tile) keys past the range load the last key instead.
-  auto issue = [&](int64_t key0, int stage, auto clamp_tag) {
+  auto issue = [&](int64_t key0, int stage, auto clamp_tag) __attribute__((always_inline)) {
     constexpr bool clamp = decltype(clamp_tag)::value;
 #pragma unroll
     for (int s = 0; s < kDmaSlots; ++s) {
@@ -287,8 +298,15 @@ __global__ void __launch_bounds__(kThreads, 2) flash_bf16_kernel(FlashParams p) 
       } else {
         src = base + key0 * row_bytes + dma_off[s];
       }
-      char* dst = lds + stage * kStage + (isk ? i * 1024 : kKTile + (i - kKInstr) * 1024);
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      char* dst = &lds[stage][isk ? i * 1024 : kKTile + (i - kKInstr) * 1024];
+      // Issued from asm: the compiler then does not make every later LDS
+      // read wait for this DMA (it cannot tell that the reads hit another
+      // stage).  Completion is awaited explicitly before each barrier.
+      const uint32_t ldsa = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                   :
+                   : "v"(src), "s"(ldsa)
+                   : "memory", "m0");
     }
   };
 
@@ -303,120 +321,272 @@ __global__ void __launch_bounds__(kThreads, 2) flash_bf16_kernel(FlashParams p) 
   const int64_t ntiles = (nkeys + kBK - 1) / kBK;
   const bf16x2 kOnes = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 
-  // One key tile.  Full tiles run without any masking; a ragged last tile
-  // (tail) runs the same body with its out-of-range keys masked to -inf.
-  auto tile_step = [&](int64_t t, auto tail_tag) {
-    constexpr bool tail = decltype(tail_tag)::value;
-    const int st = (int)(t & 1);
-    const int64_t key0 = tr.k_begin + t * kBK;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA landed
-    __syncthreads();                     // ... and every other wave's
-    if (t + 1 < ntiles) {
-      if (t + 1 == nfull)
-        issue(key0 + kBK, st ^ 1, std::true_type{});
-      else
-        issue(key0 + kBK, st ^ 1, std::false_type{});
+  // ---- building blocks on one 32-key sub-tile (sb of the tile in stage st)
+  // S^T (raw dot products) of both query blocks
+  auto qk = [&](int st, int sb, f32x16 (&S)[2]) __attribute__((always_inline)) {
+    const char* sk = &lds[st][0] + kread + sb * 32 * kKRow;
+    S[0] = 0.f;
+    S[1] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bf16x8 ka = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(sk + c * 32));
+      S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[0][c], S[0], 0, 0, 0);
+      S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[1][c], S[1], 0, 0, 0);
     }
-    const char* sk = lds + st * kStage + kread;
-    const char* sv = lds + st * kStage + vread;
-
-    // ---- S^T = scale*log2(e) * K Q^T - m for block qb and 32-key sub-tile
-    // sb; keys past the end of the range (tail tile only) get -inf.
-    auto scores = [&](int qb, int sb) {
-      f32x16 acc = 0.f;
+  };
+  // O^T += V^T P^T; the V^T operand comes from two transposed reads
+  auto pv = [&](int st, int sb, const u32x4 (&P)[2][2]) __attribute__((always_inline)) {
+    const char* sv = &lds[st][0] + vread + sb * 32 * kVRow;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bf16x8 ka = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(sk + sb * 32 * kKRow + c * 32));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[qb][c], acc, 0, 0, 0);
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const char* a = sv + 16 * c2 * kVRow + db * 64;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a);
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a + 4 * kVRow));
+        const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              va, __builtin_bit_cast(bf16x8, P[qb][c2]), o[qb][db], 0, 0, 0);
       }
-      const float nm = -m[qb];
+  };
+  // P = exp2(qscale*S - m - delta) rounded to bf16 into the PV operand;
+  // returns the lane's fp32 sum of the rounded P.  Tail: keys at or past the
+  // end of the range get P = 0.
+  auto exp_pack = [&](int qb, const f32x16& S, float delta, u32x4 (&P)[2], int64_t key0,
+                      auto tail_tag) __attribute__((always_inline)) {
+    constexpr bool tail = decltype(tail_tag)::value;
+    const float nm = -(m[qb] + delta);
+    float acc = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = __builtin_fmaf(acc[r], qscale, nm);
-      if constexpr (tail) {
+    for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t key = key0 + 32 * sb + 16 * (r >> 3) + 8 * hf + (r & 7);
-          if (key >= tr.k_end) acc[r] = -INFINITY;
+      for (int e = 0; e < 4; ++e) {
+        float z0 = __builtin_fmaf(S[8 * c2 + 2 * e], qscale, nm);
+        float z1 = __builtin_fmaf(S[8 * c2 + 2 * e + 1], qscale, nm);
+        if constexpr (tail) {
+          const int64_t k0 = key0 + 16 * c2 + 8 * hf + 2 * e;
+          if (k0 >= tr.k_end) z0 = -INFINITY;
+          if (k0 + 1 >= tr.k_end) z1 = -INFINITY;
         }
+        const uint32_t pp = pack_bf16(__builtin_amdgcn_exp2f(z0), __builtin_amdgcn_exp2f(z1));
+        P[c2][e] = pp;
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), kOnes, acc, false);
       }
-      return acc;
-    };
-    // P = exp2(S - delta) rounded to bf16 into the PV operand; returns the
-    // lane's fp32 sum of the rounded P (the values the PV product uses).
-    u32x4 pk[2][2][2];  // [qb][sb][k-chunk] bf16 P^T operands
-    auto exp_pack = [&](int qb, int sb, const f32x16& sv2, float delta) {
-      float acc = 0.f;
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(sv2[8 * c2 + 2 * e] - delta);
-          const float p1 = __builtin_amdgcn_exp2f(sv2[8 * c2 + 2 * e + 1] - delta);
-          const uint32_t pp = pack_bf16(p0, p1);
-          pk[qb][sb][c2][e] = pp;
-          acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), kOnes, acc, false);
-        }
-      return acc;
-    };
-
-    // ---- fast path: P = exp2(S) against the current reference max
+    return acc;
+  };
+  // Softmax of one sub-tile: the fast path uses the reference max m as is;
+  // the first sub-tile, or one whose probabilities sum above 2^16 in a lane,
+  // raises m to the sub-tile max (and rescales O and l) and redoes P.
+  auto softmax = [&](const f32x16 (&S)[2], u32x4 (&P)[2][2], bool first, int64_t key0,
+                     auto tail_tag) __attribute__((always_inline)) {
     float lt[2] = {0.f, 0.f};
-    bool slow = (t == 0);
+    bool slow = first;
     if (!slow) {
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) lt[qb] += exp_pack(qb, sb, scores(qb, sb), 0.f);
+      lt[0] = exp_pack(0, S[0], 0.f, P[0], key0, tail_tag);
+      lt[1] = exp_pack(1, S[1], 0.f, P[1], key0, tail_tag);
       slow = __any(!(lt[0] <= kRescaleSum && lt[1] <= kRescaleSum));
     }
-    // ---- slow path (first tile, or a tile far above the reference max):
-    // recompute S, raise m to the tile max, rescale O and l.
     if (slow) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        f32x16 sv2[2] = {scores(qb, 0), scores(qb, 1)};
-        float mx = -INFINITY;
+        float rmax = -INFINITY;
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv2[sb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float delta = mset[qb] ? fmaxf(mx, 0.f) : mx;
+        for (int r = 0; r < 16; ++r) {
+          float x = S[qb][r];
+          if constexpr (decltype(tail_tag)::value) {
+            const int64_t key = key0 + 16 * (r >> 3) + 8 * hf + (r & 7);
+            if (key >= tr.k_end) x = -INFINITY;
+          }
+          rmax = fmaxf(rmax, x);
+        }
+        rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+        const float mx = rmax == -INFINITY ? -INFINITY : __builtin_fmaf(rmax, qscale, -m[qb]);
+        // a fully masked sub-tile (tail) leaves the state unchanged
+        const float delta = mx == -INFINITY ? 0.f : (mset[qb] ? fmaxf(mx, 0.f) : mx);
         const float factor = mset[qb] ? exp2f(-delta) : 1.f;
         m[qb] += delta;
-        mset[qb] = true;
+        mset[qb] = mset[qb] || mx != -INFINITY;
         lsum[qb] *= factor;
         o[qb][0] *= factor;
         o[qb][1] *= factor;
-        lt[qb] = exp_pack(qb, 0, sv2[0], delta) + exp_pack(qb, 1, sv2[1], delta);
+        lt[qb] = exp_pack(qb, S[qb], 0.f, P[qb], key0, tail_tag);
       }
     }
     lsum[0] += lt[0];
     lsum[1] += lt[1];
-
-    // ---- O^T += V^T P^T; the V^T operand comes from two transposed reads
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          const char* a = sv + (32 * sb + 16 * c2) * kVRow + db * 64;
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a);
-          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a + 4 * kVRow));
-          const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                va, __builtin_bit_cast(bf16x8, pk[qb][sb][c2]), o[qb][db], 0, 0, 0);
-        }
   };
-  if (nfull == 0)
-    issue(tr.k_begin, 0, std::true_type{});
+
+  // Steady-state step, fast path, unit by unit: QK of the next sub-tile
+  // (K at stK/sbK) and PV of the previous one (V at stV/sbV, operand Pp)
+  // on the matrix core, each MFMA followed by one pair of this sub-tile's
+  // softmax (scores Sc -> Pc); the sched barriers pin that order.  Returns
+  // the lane sums of the rounded P in lt.
+  auto step_fast = [&](int stK, int sbK, int stV, int sbV, const f32x16 (&Sc)[2],
+                       u32x4 (&Pc)[2][2], f32x16 (&Sn)[2], const u32x4 (&Pp)[2][2],
+                       float (&lt)[2]) __attribute__((always_inline)) {
+    const char* sk = &lds[stK][0] + kread + sbK * 32 * kKRow;
+    const char* sv = &lds[stV][0] + vread + sbV * 32 * kVRow;
+    // PV units first (they free Pp), then the QK units (they fill Sn); the
+    // operand of each MFMA pair is read from LDS two units ahead
+    bf16x8 va[2][2], ka[4];
+    auto load_v = [&](int db, int c2) __attribute__((always_inline)) {
+      const char* a = sv + 16 * c2 * kVRow + db * 64;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a);
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a + 4 * kVRow));
+      va[db][c2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto load_k = [&](int c) __attribute__((always_inline)) {
+      ka[c] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(sk + c * 32));
+    };
+    const float nm0 = -m[0], nm1 = -m[1];
+    lt[0] = 0.f;
+    lt[1] = 0.f;
+    auto pair = [&](int u) __attribute__((always_inline)) {
+      const int qb = u >> 3, c2 = (u >> 2) & 1, e = u & 3;
+      const float nm = qb ? nm1 : nm0;
+      const float z0 = __builtin_fmaf(Sc[qb][8 * c2 + 2 * e], qscale, nm);
+      const float z1 = __builtin_fmaf(Sc[qb][8 * c2 + 2 * e + 1], qscale, nm);
+      const uint32_t pp = pack_bf16(__builtin_amdgcn_exp2f(z0), __builtin_amdgcn_exp2f(z1));
+      Pc[qb][c2][e] = pp;
+      lt[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), kOnes, lt[qb], false);
+    };
+    load_v(0, 0);
+    load_v(0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      // PV unit: operand (db, c2) for query block qb
+      const int db = u >> 2, c2 = (u >> 1) & 1, qb = u & 1;
+      if (u == 1) load_v(1, 0);
+      if (u == 3) load_v(1, 1);
+      if (u == 5) load_k(0);
+      if (u == 6) load_k(1);
+      pair(u);
+      o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][c2], __builtin_bit_cast(bf16x8, Pp[qb][c2]),
+                                                          o[qb][db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int u = 8; u < 16; ++u) {
+      // QK unit: k-step c for query block qb
+      const int w = u - 8, c = w >> 1, qb = w & 1;
+      if (w == 1) load_k(2);
+      if (w == 3) load_k(3);
+      pair(u);
+      Sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qreg[qb][c], c == 0 ? f32x16(0.f) : Sn[qb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // the rare exact redo after a fast step: raise m to the sub-tile max
+  // (O and l rescaled) and recompute P
+  auto redo_exact = [&](const f32x16 (&S)[2], u32x4 (&P)[2][2], float (&lt)[2])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float rmax = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, S[qb][r]);
+      rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+      const float mx = __builtin_fmaf(rmax, qscale, -m[qb]);
+      const float delta = mset[qb] ? fmaxf(mx, 0.f) : mx;
+      const float factor = mset[qb] ? exp2f(-delta) : 1.f;
+      m[qb] += delta;
+      mset[qb] = true;
+      lsum[qb] *= factor;
+      o[qb][0] *= factor;
+      o[qb][1] *= factor;
+      lt[qb] = exp_pack(qb, S[qb], 0.f, P[qb], 0, std::false_type{});
+    }
+  };
+
+  // ---- software pipeline over 32-key sub-tiles j (two per LDS tile): step j
+  // runs QK of sub-tile j+1 and PV of sub-tile j-1 on the matrix core while
+  // the VALU computes the softmax of sub-tile j.  Three LDS stages: tile t+2
+  // loads into the stage of tile t-1, whose last reader (PV of its second
+  // sub-tile) ran before the barrier that precedes the load.
+  f32x16 Sa[2], Sb[2];
+  u32x4 Pa[2][2], Pb[2][2];
+  // Tile order: the ragged tail first (if any), then the full tiles; the
+  // softmax sums do not depend on the key order.
+  const bool has_tail = ntiles > nfull;
+  auto tile_key0 = [&](int64_t i) __attribute__((always_inline)) {
+    return has_tail ? (i == 0 ? tr.k_begin + nfull * kBK : tr.k_begin + (i - 1) * kBK)
+                    : tr.k_begin + i * kBK;
+  };
+  auto issue_tile = [&](int64_t i, int st) __attribute__((always_inline)) {
+    if (has_tail && i == 0)
+      issue(tile_key0(0), st, std::true_type{});
+    else
+      issue(tile_key0(i), st, std::false_type{});
+  };
+  issue_tile(0, 0);
+  if (ntiles > 1) issue_tile(1, 1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  // step 0: QK(0), QK(1), exact softmax of sub-tile 0 (masked if tile 0 is
+  // the tail)
+  const int64_t key00 = tile_key0(0);
+  qk(0, 0, Sa);
+  qk(0, 1, Sb);
+  if (has_tail)
+    softmax(Sa, Pa, true, key00, std::true_type{});
   else
-    issue(tr.k_begin, 0, std::false_type{});
-  for (int64_t t = 0; t < nfull; ++t) tile_step(t, std::false_type{});
-  if (ntiles > nfull) tile_step(nfull, std::true_type{});
+    softmax(Sa, Pa, true, key00, std::false_type{});
+  // fast pipeline step: QK -> Sn (stage stK, sub sbK), PV of Pp (stage stV,
+  // sub sbV), softmax Sc -> Pc of the full sub-tile in stage stC, sub sbC
+  auto step = [&](int stK, int sbK, int stV, int sbV, int stC, int sbC, const f32x16 (&Sc)[2],
+                  u32x4 (&Pc)[2][2], f32x16 (&Sn)[2], const u32x4 (&Pp)[2][2])
+      __attribute__((always_inline)) {
+    float lt[2];
+    step_fast(stK, sbK, stV, sbV, Sc, Pc, Sn, Pp, lt);
+    if (__any(!(lt[0] <= kRescaleSum && lt[1] <= kRescaleSum))) {
+      // rare: recompute this sub-tile's scores (its tile is still in LDS)
+      f32x16 Sr[2];
+      qk(stC, sbC, Sr);
+      redo_exact(Sr, Pc, lt);
+    }
+    lsum[0] += lt[0];
+    lsum[1] += lt[1];
+  };
+  // tile t+1 must have landed before its first QK; tile t+2 then loads into
+  // the stage of tile t-1
+  auto advance = [&](int64_t t, int st_prev) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (t + 2 < ntiles) issue_tile(t + 2, st_prev);
+  };
+  int st = 0;
+  if (ntiles > 1) {
+    // tile 0 (plain order; its second sub-tile may be masked)
+    advance(0, kStages - 1);
+    qk(1, 0, Sa);
+    pv(0, 0, Pa);
+    if (has_tail)
+      softmax(Sb, Pb, false, key00 + 32, std::true_type{});
+    else
+      softmax(Sb, Pb, false, key00 + 32, std::false_type{});
+    step(1, 1, 0, 1, 1, 0, Sa, Pa, Sb, Pb);  // QK(3) | PV(1) | softmax(2)
+    // full tiles 1 .. ntiles-2
+    st = 1;
+    for (int64_t t = 1; t + 1 < ntiles; ++t) {
+      const int st_prev = st == 0 ? kStages - 1 : st - 1;
+      const int st_next = st == kStages - 1 ? 0 : st + 1;
+      advance(t, st_prev);
+      step(st_next, 0, st, 0, st, 1, Sb, Pb, Sa, Pa);       // QK(2t+2) | PV(2t) | softmax(2t+1)
+      step(st_next, 1, st, 1, st_next, 0, Sa, Pa, Sb, Pb);  // QK(2t+3) | PV(2t+1) | softmax(2t+2)
+      st = st_next;
+    }
+  }
+  // last tile: PV(2t), softmax(2t+1) (masked if it is the only tile and the
+  // tail), PV(2t+1)
+  pv(st, 0, Pa);
+  if (ntiles == 1 && has_tail)
+    softmax(Sb, Pb, false, key00 + 32, std::true_type{});
+  else
+    softmax(Sb, Pb, false, 0, std::false_type{});
+  pv(st, 1, Pb);
 
   // ---- normalise and store O (bf16, RNE)
   uint16_t* __restrict__ og = (uint16_t*)p.o;
