@@ -144,6 +144,10 @@ SHAPES = [
     (5, 11, 13, 4, 2),    # L = 147 spans several 64-key tiles, T = 735 several q tiles
     (1, 16, 16, 0, 1),    # L = 256: exactly one query tile
     (2, 16, 16, 1, 1),    # L = 257: one row past a tile
+    (2, 8, 8, 0, 1),      # L = 64: exactly one key tile, no ragged tile
+    (2, 4, 8, 0, 2),      # L = 32: one ragged tile whose second half is empty
+    (1, 8, 12, 0, 1),     # L = 96: a ragged 32-key tile plus one full tile
+    (3, 5, 13, 0, 1),     # L = 65: a one-key ragged tile plus one full tile
 ]
 
 
