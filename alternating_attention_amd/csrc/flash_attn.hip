@@ -11,8 +11,8 @@
 //              (own token, when dropped) and the count-weighted mean column,
 //              so the three parts share one softmax.
 //
-// bf16 path (MFMA).  A workgroup of 4 waves owns 256 queries of one head;
-// each wave owns 64 queries as two 32-query blocks.  Scores are computed
+// bf16 path (MFMA).  A workgroup of 8 waves (two per SIMD) owns 512 queries
+// of one head; each wave owns 64 queries as two 32-query blocks.  Scores are computed
 // transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: keys index the
 // accumulator rows and queries its columns, so every lane holds 16 scores of
 // ONE query.  Row statistics therefore stay in the lane (plus its partner
@@ -22,19 +22,20 @@
 // register r of lane half h holds key 16*(r/8) + 8*h + r%8 -- exactly the
 // B-operand k-slot order of the PV product.  V stays in its natural layout;
 // the PV A operand (V^T) comes from ds_read_b64_tr_b16 transposed reads.
-// K/V tiles of 64 keys move global -> LDS with global_load_lds_dwordx4 (no
-// registers) through a ring of three stages; a ragged last tile is taken
-// first (softmax sums do not depend on the key order), so every later tile
-// is full and needs no masking.
+// K/V tiles of 128 keys move global -> LDS with global_load_lds_dwordx4 (no
+// registers) through a ring of three stages (114 KB: one workgroup per CU);
+// a ragged last tile is taken first (softmax sums do not depend on the key
+// order), so every later tile is full and needs no masking.
 //
 // Software pipeline over 32-key sub-tiles j: step j issues the QK^T MFMAs
 // of sub-tile j+1 and the PV MFMAs of sub-tile j-1 while the VALU computes
 // the softmax of sub-tile j; the three are independent, and sched barriers
 // interleave them one MFMA to one pair of scores, so the matrix core and
 // the VALU of one wave run side by side (a second wave per SIMD fills the
-// gaps).  Each tile costs one barrier: tile t+1 must have landed before its
-// first QK, and tile t+2 then loads into the stage of tile t-1, whose last
-// reader (the PV of its second sub-tile) ran before that barrier.
+// gaps).  Each tile (four steps) costs one barrier, before its fourth step:
+// tile t+1 must have landed before its first QK, and tile t+2 then loads
+// into the stage of tile t-1, whose last reader (the PV of its last
+// sub-tile, in the first step of tile t) ran before that barrier.
 //
 // Softmax: the MFMA produces exact fp32 dot products of the bf16 rows; one
 // FMA per score turns them into log2 units and subtracts the row's
@@ -61,10 +62,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;          // 4 waves
+constexpr int kThreads = 512;          // 8 waves
 constexpr int kQPerWave = 64;
-constexpr int kBQ = 4 * kQPerWave;     // queries per workgroup
-constexpr int kBK = 64;                // keys per LDS tile
+constexpr int kBQ = 8 * kQPerWave;     // queries per workgroup
+constexpr int kBK = 128;               // keys per LDS tile (4 sub-tiles of 32)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSum = 65536.f;  // lazy-rescale trigger (2^16)
 
@@ -135,18 +136,18 @@ __device__ __forceinline__ bool sga_kept(const SgaGrid& g, int64_t t) {
   return (r % g.sh == g.oh) && (c % g.sw == g.ow);
 }
 
-// LDS tiles.  K: 64 rows of 128 bytes padded to 144 (row i of a 32-key
-// sub-tile holds key perm_row(i)); V: 64 rows (natural key order) padded to
+// LDS tiles.  K: 128 rows of 128 bytes padded to 144 (row i of a 32-key
+// sub-tile holds key perm_row(i)); V: 128 rows (natural key order) padded to
 // 160 bytes.  The padding spreads the rows that one LDS read touches over
 // distinct banks, and keeps every read address a per-lane base plus an
 // immediate.  Both tiles are filled by global_load_lds_dwordx4 (global ->
 // LDS without registers), 1 KB (64 x 16 bytes) per instruction; granules
 // that fall in the padding load a harmless in-range duplicate.
 constexpr int kKRow = 144, kVRow = 160;
-constexpr int kKTile = kBK * kKRow, kVTile = kBK * kVRow;     // 9216, 10240
-constexpr int kStage = kKTile + kVTile;                        // 19456
-constexpr int kKInstr = kKTile / 1024, kVInstr = kVTile / 1024;  // 9, 10
-constexpr int kDmaSlots = (kKInstr + kVInstr + 3) / 4;         // per wave: 5
+constexpr int kKTile = kBK * kKRow, kVTile = kBK * kVRow;     // 18432, 20480
+constexpr int kStage = kKTile + kVTile;                        // 38912
+constexpr int kKInstr = kKTile / 1024, kVInstr = kVTile / 1024;  // 18, 20
+constexpr int kDmaSlots = (kKInstr + kVInstr + 7) / 8;         // per wave: 5
 constexpr int kStages = 3;
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -154,7 +155,7 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 template <KeyRange KR>
-__global__ void __launch_bounds__(kThreads, 2) flash_bf16_kernel(FlashParams p) {
+__global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) {
   __shared__ __attribute__((aligned(16))) char lds[kStages][kStage];
 
   const TileRange tr = tile_range<KR>(p);
@@ -253,13 +254,13 @@ __global__ void __launch_bounds__(kThreads, 2) flash_bf16_kernel(FlashParams p) 
     }
   }
 
-  // ---- DMA plan: wave w issues the tile's 1 KB instructions w, w+4, ...
-  // (0..8: K, 9..18: V).  A lane's granule: key offset within the tile and
+  // ---- DMA plan: wave w issues the tile's 1 KB instructions w, w+8, ...
+  // (0..17: K, 18..37: V).  A lane's granule: key offset within the tile and
   // byte offset within the row.
   auto dma_granule = [&](int i, int& key, uint32_t& col) {
     if (i < kKInstr) {
       const int g = i * 64 + lane, row = g / 9, gc = g % 9;
-      key = (row & 32) + perm_row(row & 31);
+      key = (row & ~31) + perm_row(row & 31);
       col = gc < 8 ? gc * 16 : 0;
     } else {
       const int g = (i - kKInstr) * 64 + lane, row = g / 10, gc = g % 10;
@@ -272,7 +273,7 @@ __global__ void __launch_bounds__(kThreads, 2) flash_bf16_kernel(FlashParams p) 
   for (int s = 0; s < kDmaSlots; ++s) {
     int key;
     uint32_t col;
-    dma_granule(4 * s + wave, key, col);
+    dma_granule(8 * s + wave, key, col);
     dma_off[s] = (uint32_t)key * (uint32_t)row_bytes + col;
   }
   const char* kbytes = (const char*)p.k + (int64_t)head * 128;
@@ -283,7 +284,7 @@ __global__ void __launch_bounds__(kThreads, 2) flash_bf16_kernel(FlashParams p) 
     constexpr bool clamp = decltype(clamp_tag)::value;
 #pragma unroll
     for (int s = 0; s < kDmaSlots; ++s) {
-      const int i = 4 * s + wave;
+      const int i = 8 * s + wave;
       if (i >= kKInstr + kVInstr) continue;
       const bool isk = i < kKInstr;
       const char* base = isk ? kbytes : vbytes;
@@ -525,15 +526,6 @@ __global__ void __launch_bounds__(kThreads, 2) flash_bf16_kernel(FlashParams p) 
   if (ntiles > 1) issue_tile(1, 1);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  // step 0: QK(0), QK(1), exact softmax of sub-tile 0 (masked if tile 0 is
-  // the tail)
-  const int64_t key00 = tile_key0(0);
-  qk(0, 0, Sa);
-  qk(0, 1, Sb);
-  if (has_tail)
-    softmax(Sa, Pa, true, key00, std::true_type{});
-  else
-    softmax(Sa, Pa, true, key00, std::false_type{});
   // fast pipeline step: QK -> Sn (stage stK, sub sbK), PV of Pp (stage stV,
   // sub sbV), softmax Sc -> Pc of the full sub-tile in stage stC, sub sbC
   auto step = [&](int stK, int sbK, int stV, int sbV, int stC, int sbC, const f32x16 (&Sc)[2],
@@ -550,6 +542,14 @@ __global__ void __launch_bounds__(kThreads, 2) flash_bf16_kernel(FlashParams p) 
     lsum[0] += lt[0];
     lsum[1] += lt[1];
   };
+  // the same step in plain order, masking the sub-tile at key0 (tail tile)
+  auto step_tail = [&](int stK, int sbK, int stV, int sbV, const f32x16 (&Sc)[2],
+                       u32x4 (&Pc)[2][2], f32x16 (&Sn)[2], const u32x4 (&Pp)[2][2], int64_t key0)
+      __attribute__((always_inline)) {
+    qk(stK, sbK, Sn);
+    pv(stV, sbV, Pp);
+    softmax(Sc, Pc, false, key0, std::true_type{});
+  };
   // tile t+1 must have landed before its first QK; tile t+2 then loads into
   // the stage of tile t-1
   auto advance = [&](int64_t t, int st_prev) __attribute__((always_inline)) {
@@ -557,36 +557,40 @@ __global__ void __launch_bounds__(kThreads, 2) flash_bf16_kernel(FlashParams p) 
     __syncthreads();
     if (t + 2 < ntiles) issue_tile(t + 2, st_prev);
   };
-  int st = 0;
-  if (ntiles > 1) {
-    // tile 0 (plain order; its second sub-tile may be masked)
-    advance(0, kStages - 1);
-    qk(1, 0, Sa);
-    pv(0, 0, Pa);
-    if (has_tail)
-      softmax(Sb, Pb, false, key00 + 32, std::true_type{});
-    else
-      softmax(Sb, Pb, false, key00 + 32, std::false_type{});
-    step(1, 1, 0, 1, 1, 0, Sa, Pa, Sb, Pb);  // QK(3) | PV(1) | softmax(2)
-    // full tiles 1 .. ntiles-2
-    st = 1;
-    for (int64_t t = 1; t + 1 < ntiles; ++t) {
-      const int st_prev = st == 0 ? kStages - 1 : st - 1;
-      const int st_next = st == kStages - 1 ? 0 : st + 1;
-      advance(t, st_prev);
-      step(st_next, 0, st, 0, st, 1, Sb, Pb, Sa, Pa);       // QK(2t+2) | PV(2t) | softmax(2t+1)
-      step(st_next, 1, st, 1, st_next, 0, Sa, Pa, Sb, Pb);  // QK(2t+3) | PV(2t+1) | softmax(2t+2)
-      st = st_next;
-    }
+  // ---- tile 0 (the ragged tail when there is one): steps 0..3
+  const int64_t key00 = tile_key0(0);
+  const int st1 = ntiles > 1 ? 1 : 0;  // QK target of step 3 (a dummy re-read if no tile 1)
+  qk(0, 0, Sa);
+  if (has_tail) {
+    qk(0, 1, Sb);
+    softmax(Sa, Pa, true, key00, std::true_type{});
+    step_tail(0, 2, 0, 0, Sb, Pb, Sa, Pa, key00 + 32);
+    step_tail(0, 3, 0, 1, Sa, Pa, Sb, Pb, key00 + 64);
+    if (ntiles > 1) advance(0, kStages - 1);
+    step_tail(st1, 0, 0, 2, Sb, Pb, Sa, Pa, key00 + 96);
+  } else {
+    qk(0, 1, Sb);
+    softmax(Sa, Pa, true, key00, std::false_type{});
+    step(0, 2, 0, 0, 0, 1, Sb, Pb, Sa, Pa);
+    step(0, 3, 0, 1, 0, 2, Sa, Pa, Sb, Pb);
+    if (ntiles > 1) advance(0, kStages - 1);
+    step(st1, 0, 0, 2, 0, 3, Sb, Pb, Sa, Pa);
   }
-  // last tile: PV(2t), softmax(2t+1) (masked if it is the only tile and the
-  // tail), PV(2t+1)
-  pv(st, 0, Pa);
-  if (ntiles == 1 && has_tail)
-    softmax(Sb, Pb, false, key00 + 32, std::true_type{});
-  else
-    softmax(Sb, Pb, false, 0, std::false_type{});
-  pv(st, 1, Pb);
+  // ---- full tiles 1 .. ntiles-1: steps 4t .. 4t+3
+  int st = 0;
+  for (int64_t t = 1; t < ntiles; ++t) {
+    const int st_prev = st;
+    st = st == kStages - 1 ? 0 : st + 1;
+    const int st_next = st == kStages - 1 ? 0 : st + 1;
+    const bool has_next = t + 1 < ntiles;
+    step(st, 1, st_prev, 3, st, 0, Sa, Pa, Sb, Pb);  // QK(t,1) | PV(t-1,3) | softmax(t,0)
+    step(st, 2, st, 0, st, 1, Sb, Pb, Sa, Pa);       // QK(t,2) | PV(t,0)   | softmax(t,1)
+    step(st, 3, st, 1, st, 2, Sa, Pa, Sb, Pb);       // QK(t,3) | PV(t,1)   | softmax(t,2)
+    if (has_next) advance(t, st_prev);
+    // QK(t+1,0) | PV(t,2) | softmax(t,3); the QK re-reads this tile when t is last
+    step(has_next ? st_next : st, 0, st, 2, st, 3, Sb, Pb, Sa, Pa);
+  }
+  pv(st, 3, Pb);  // drain
 
   // ---- normalise and store O (bf16, RNE)
   uint16_t* __restrict__ og = (uint16_t*)p.o;

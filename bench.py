@@ -149,6 +149,24 @@ def measured_traffic(kernel):
     return k["hbm_bytes"] if k else None
 
 
+def gpu_state():
+    """Clocks and power of the GPUs as rocm-smi reports them (best effort:
+    None when the tool is missing or prints no JSON)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"],
+                           capture_output=True, text=True, timeout=20)
+        rec = json.loads(r.stdout)
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+    keep = {}
+    for card, vals in rec.items():
+        if isinstance(vals, dict):
+            keep[card] = {k: v for k, v in vals.items()
+                          if any(w in k.lower() for w in ("sclk", "mclk", "fclk", "power"))}
+    return keep or None
+
+
 def host_bits(t, torch):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
@@ -303,6 +321,7 @@ def run(args):
     else:
         raise SystemExit("unknown workload")
 
+    state_before = gpu_state()
     log("warmup %d" % args.warmup)
     for _ in range(args.warmup):
         step()
@@ -321,6 +340,7 @@ def run(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / args.steps
+    state_after = gpu_state()
 
     per = {}
     for name, t in timers.items():
@@ -328,7 +348,8 @@ def run(args):
         calls_per_step = len(ms) / args.steps
         avg = float(np.mean(ms))
         flop = work[name] / calls_per_step
-        per[name] = {"ms_per_call": avg, "calls_per_step": calls_per_step,
+        per[name] = {"ms_per_call": avg, "ms_median": float(np.median(ms)), "ms_min": float(min(ms)),
+                     "calls_per_step": calls_per_step,
                      "tflops": flop / (avg * 1e-3) / 1e12,
                      "frac_mfma_peak": flop / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                      "tokens_per_s": T / (avg * 1e-3)}
@@ -443,6 +464,7 @@ def run(args):
         "config": {"workload": desc, "frames": N, "tokens_per_frame": L, "tokens": T,
                    "heads": H, "head_dim": HEAD_DIM},
         "roofline": roofline, "modes": per, "wall_s_timed": wall,
+        "gpu_state": {"before": state_before, "after": state_after},
     }
     result.update(extra)
     if not args.no_cpu_baseline:
