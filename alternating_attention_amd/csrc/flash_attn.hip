@@ -5,17 +5,17 @@
 // "AVGGT: Rethinking Global Attention for Accelerating VGGT", section 3):
 //   kFrame  -- the keys of a query are the L tokens of its own frame;
 //   kGlobal -- the keys are all T tokens; the T x T score matrix only ever
-//              exists one 64-key tile at a time in registers;
+//              exists one 32-key sub-tile at a time in registers;
 //   kSga    -- the keys are the compacted kept rows (Kc, Vc), and the
 //              softmax state of each query starts from its diagonal column
-//              (own token, when dropped) and the count-weighted mean column,
-//              so the three parts share one softmax.
+//              (own token, when dropped) and the mean column (count-weighted
+//              or unit weight), so the three parts share one softmax.
 //
 // bf16 path (MFMA).  A workgroup of 8 waves (two per SIMD) owns 512 queries
-// of one head; each wave owns 64 queries as two 32-query blocks.  Scores are computed
-// transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: keys index the
-// accumulator rows and queries its columns, so every lane holds 16 scores of
-// ONE query.  Row statistics therefore stay in the lane (plus its partner
+// of one head; each wave owns 64 queries as two 32-query blocks.  Scores are
+// computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: keys
+// index the accumulator rows and queries its columns, so every lane holds
+// 16 scores of ONE query.  Row statistics therefore stay in the lane (plus its partner
 // lane l^32); the probabilities P^T feed O^T = V^T P^T directly as the B
 // operand without touching LDS.  K rows are stored in LDS in a permuted
 // order (bits 2 and 3 of the row index swapped) so that accumulator
@@ -179,7 +179,8 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
     const int64_t row = min(tr.q_begin + wave * kQPerWave + qb * 32 + l32, tr.q_end - 1);
     const uint16_t* src = qg + ((size_t)row * H + head) * 64 + 8 * hf;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qreg[qb][c] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + 16 * c));
+    for (int c = 0; c < 4; ++c)
+      qreg[qb][c] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + 16 * c));
   }
 
   // ---- softmax state.  Lane (l32, hf) of block qb holds, for its query:
@@ -278,7 +279,7 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
   }
   const char* kbytes = (const char*)p.k + (int64_t)head * 128;
   const char* vbytes = (const char*)p.v + (int64_t)head * 128;
-  // Issue the DMA of the tile at key0 into `stage`; with clamp (ragged last
+  // Issue the DMA of the tile at key0 into `stage`; with clamp (the ragged
   // tile) keys past the range load the last key instead.
   auto issue = [&](int64_t key0, int stage, auto clamp_tag) __attribute__((always_inline)) {
     constexpr bool clamp = decltype(clamp_tag)::value;
@@ -302,7 +303,10 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
       char* dst = &lds[stage][isk ? i * 1024 : kKTile + (i - kKInstr) * 1024];
       // Issued from asm: the compiler then does not make every later LDS
       // read wait for this DMA (it cannot tell that the reads hit another
-      // stage).  Completion is awaited explicitly before each barrier.
+      // stage).  Completion is awaited explicitly before each barrier.  The
+      // instruction writes LDS only and has no destination registers, so no
+      // register can be reused while it is in flight; its address
+      // registers are read at issue (as for the builtin form).
       const uint32_t ldsa = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
       asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                    :
@@ -451,7 +455,8 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
       const float z1 = __builtin_fmaf(Sc[qb][8 * c2 + 2 * e + 1], qscale, nm);
       const uint32_t pp = pack_bf16(__builtin_amdgcn_exp2f(z0), __builtin_amdgcn_exp2f(z1));
       Pc[qb][c2][e] = pp;
-      lt[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), kOnes, lt[qb], false);
+      lt[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), kOnes, lt[qb],
+                                               false);
     };
     load_v(0, 0);
     load_v(0, 1);
@@ -465,8 +470,8 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
       if (u == 5) load_k(0);
       if (u == 6) load_k(1);
       pair(u);
-      o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][c2], __builtin_bit_cast(bf16x8, Pp[qb][c2]),
-                                                          o[qb][db], 0, 0, 0);
+      o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          va[db][c2], __builtin_bit_cast(bf16x8, Pp[qb][c2]), o[qb][db], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -476,7 +481,8 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
       if (w == 1) load_k(2);
       if (w == 3) load_k(3);
       pair(u);
-      Sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qreg[qb][c], c == 0 ? f32x16(0.f) : Sn[qb], 0, 0, 0);
+      Sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qreg[qb][c],
+                                                       c == 0 ? f32x16(0.f) : Sn[qb], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -502,11 +508,11 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
     }
   };
 
-  // ---- software pipeline over 32-key sub-tiles j (two per LDS tile): step j
-  // runs QK of sub-tile j+1 and PV of sub-tile j-1 on the matrix core while
-  // the VALU computes the softmax of sub-tile j.  Three LDS stages: tile t+2
-  // loads into the stage of tile t-1, whose last reader (PV of its second
-  // sub-tile) ran before the barrier that precedes the load.
+  // ---- software pipeline over 32-key sub-tiles j (four per LDS tile): step
+  // j runs QK of sub-tile j+1 and PV of sub-tile j-1 on the matrix core
+  // while the VALU computes the softmax of sub-tile j.  Three LDS stages:
+  // tile t+2 loads into the stage of tile t-1, whose last reader (the PV of
+  // its last sub-tile) ran before the barrier that precedes the load.
   f32x16 Sa[2], Sb[2];
   u32x4 Pa[2][2], Pb[2][2];
   // Tile order: the ragged tail first (if any), then the full tiles; the
@@ -699,7 +705,6 @@ __global__ void __launch_bounds__(kF32Threads) flash_f32_kernel(FlashParams p) {
   for (int e = 0; e < 64; ++e) og[e] = acc[e] * inv;
 }
 
-template <typename KernelT>
 int64_t blocks_for(KeyRange kr, const FlashParams& p, int rows_per_block) {
   if (kr == KeyRange::kFrame)
     return (int64_t)p.H * p.num_frames * ((p.L + rows_per_block - 1) / rows_per_block);
@@ -709,25 +714,37 @@ int64_t blocks_for(KeyRange kr, const FlashParams& p, int rows_per_block) {
 }  // namespace
 
 hipError_t launch_flash_bf16(KeyRange kr, const FlashParams& p, hipStream_t s) {
-  const int64_t nb = blocks_for<void>(kr, p, kBQ);
+  const int64_t nb = blocks_for(kr, p, kBQ);
   if (nb <= 0) return hipSuccess;
   const dim3 grid((uint32_t)nb), block(kThreads);
   switch (kr) {
-    case KeyRange::kFrame: hipLaunchKernelGGL(flash_bf16_kernel<KeyRange::kFrame>, grid, block, 0, s, p); break;
-    case KeyRange::kGlobal: hipLaunchKernelGGL(flash_bf16_kernel<KeyRange::kGlobal>, grid, block, 0, s, p); break;
-    case KeyRange::kSga: hipLaunchKernelGGL(flash_bf16_kernel<KeyRange::kSga>, grid, block, 0, s, p); break;
+    case KeyRange::kFrame:
+      hipLaunchKernelGGL(flash_bf16_kernel<KeyRange::kFrame>, grid, block, 0, s, p);
+      break;
+    case KeyRange::kGlobal:
+      hipLaunchKernelGGL(flash_bf16_kernel<KeyRange::kGlobal>, grid, block, 0, s, p);
+      break;
+    case KeyRange::kSga:
+      hipLaunchKernelGGL(flash_bf16_kernel<KeyRange::kSga>, grid, block, 0, s, p);
+      break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_flash_f32(KeyRange kr, const FlashParams& p, hipStream_t s) {
-  const int64_t nb = blocks_for<void>(kr, p, kF32Threads);
+  const int64_t nb = blocks_for(kr, p, kF32Threads);
   if (nb <= 0) return hipSuccess;
   const dim3 grid((uint32_t)nb), block(kF32Threads);
   switch (kr) {
-    case KeyRange::kFrame: hipLaunchKernelGGL(flash_f32_kernel<KeyRange::kFrame>, grid, block, 0, s, p); break;
-    case KeyRange::kGlobal: hipLaunchKernelGGL(flash_f32_kernel<KeyRange::kGlobal>, grid, block, 0, s, p); break;
-    case KeyRange::kSga: hipLaunchKernelGGL(flash_f32_kernel<KeyRange::kSga>, grid, block, 0, s, p); break;
+    case KeyRange::kFrame:
+      hipLaunchKernelGGL(flash_f32_kernel<KeyRange::kFrame>, grid, block, 0, s, p);
+      break;
+    case KeyRange::kGlobal:
+      hipLaunchKernelGGL(flash_f32_kernel<KeyRange::kGlobal>, grid, block, 0, s, p);
+      break;
+    case KeyRange::kSga:
+      hipLaunchKernelGGL(flash_f32_kernel<KeyRange::kSga>, grid, block, 0, s, p);
+      break;
   }
   return hipGetLastError();
 }

@@ -131,19 +131,29 @@ def cpu_baseline(workload, frames, sga_list, modes, qkv_host, rows_count, seed=7
             "seconds_per_step": step_s}
 
 
+def code_digest(path):
+    """sha256 of a source file's code: comments and all whitespace removed,
+    so that edits to comments or layout keep the digest."""
+    import hashlib
+    import re
+    text = open(path, encoding="utf-8").read()
+    tok = re.compile(r'"(?:\\.|[^"\\])*"|//[^\n]*|/\*.*?\*/', re.S)
+    text = tok.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", text)
+    return hashlib.sha256(re.sub(r"\s+", "", text).encode()).hexdigest()
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (FETCH_SIZE/WRITE_SIZE scaled by a plain copy), or None when the
-    kernel source changed since the counters were taken."""
-    import hashlib
+    kernel code changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic_n100.json")
     src = os.path.join(ROOT, "alternating_attention_amd", "csrc", "flash_attn.hip")
     try:
         rec = json.load(open(path))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        digest = code_digest(src)
     except (OSError, ValueError):
         return None
-    if rec.get("sources_sha256", {}).get("flash_attn.hip") != sha:
+    if rec.get("sources_code_digest", {}).get("flash_attn.hip") != digest:
         return None
     k = rec.get("kernels", {}).get(kernel)
     return k["hbm_bytes"] if k else None
@@ -321,7 +331,7 @@ def run(args):
     else:
         raise SystemExit("unknown workload")
 
-    state_before = gpu_state()
+    state_before = None if args.no_gpu_state else gpu_state()
     log("warmup %d" % args.warmup)
     for _ in range(args.warmup):
         step()
@@ -340,7 +350,7 @@ def run(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    state_after = gpu_state()
+    state_after = None if args.no_gpu_state else gpu_state()
 
     per = {}
     for name, t in timers.items():
@@ -498,6 +508,8 @@ def main():
                     choices=["n100", "n300", "n800", "n800reg", "shard8", "sweep"])
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gpu-state", action="store_true",
+                    help="skip the rocm-smi clock query (for runs under a profiler)")
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
