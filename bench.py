@@ -159,22 +159,60 @@ def measured_traffic(kernel):
     return k["hbm_bytes"] if k else None
 
 
-def gpu_state():
-    """Clocks and power of the GPUs as rocm-smi reports them (best effort:
-    None when the tool is missing or prints no JSON)."""
+def smi_sample():
+    """Socket power (W) and the engine clock of each XCD (MHz) as amd-smi
+    reports them (best effort: None when the tool is missing or fails)."""
+    import re
     import subprocess
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"],
+        r = subprocess.run(["amd-smi", "metric", "--power", "--clock"],
                            capture_output=True, text=True, timeout=20)
-        rec = json.loads(r.stdout)
-    except (OSError, ValueError, subprocess.SubprocessError):
+    except (OSError, subprocess.SubprocessError):
         return None
-    keep = {}
-    for card, vals in rec.items():
-        if isinstance(vals, dict):
-            keep[card] = {k: v for k, v in vals.items()
-                          if any(w in k.lower() for w in ("sclk", "mclk", "fclk", "power"))}
-    return keep or None
+    pw = re.search(r"SOCKET_POWER:\s*([\d.]+)\s*W", r.stdout)
+    clk = [float(c) for c in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([\d.]+)\s*MHz", r.stdout)]
+    if pw is None and not clk:
+        return None
+    return {"socket_power_w": float(pw.group(1)) if pw else None, "gfx_clk_mhz": clk}
+
+
+class SmiWatch:
+    """Samples smi_sample() in a background thread while the timed region
+    runs, so that the report shows the power and clock the work ran at."""
+
+    def __init__(self, enabled):
+        import threading
+        self.enabled, self.samples = enabled, []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._loop, daemon=True)
+
+    def _loop(self):
+        while not self._stop.is_set():
+            rec = smi_sample()
+            if rec is None:
+                return
+            self.samples.append(rec)
+            self._stop.wait(0.25)
+
+    def __enter__(self):
+        if self.enabled:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.enabled:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        pw = sorted(x["socket_power_w"] for x in self.samples if x["socket_power_w"] is not None)
+        clk = sorted(float(np.mean(x["gfx_clk_mhz"])) for x in self.samples if x["gfx_clk_mhz"])
+        if not pw and not clk:
+            return None
+        return {"samples": len(self.samples),
+                "socket_power_w_median": pw[len(pw) // 2] if pw else None,
+                "socket_power_w_max": pw[-1] if pw else None,
+                "gfx_clk_mhz_median": clk[len(clk) // 2] if clk else None}
 
 
 def host_bits(t, torch):
@@ -331,7 +369,7 @@ def run(args):
     else:
         raise SystemExit("unknown workload")
 
-    state_before = None if args.no_gpu_state else gpu_state()
+    state_before = None if args.no_gpu_state else smi_sample()
     log("warmup %d" % args.warmup)
     for _ in range(args.warmup):
         step()
@@ -341,16 +379,17 @@ def run(args):
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record()
-    for i in range(args.steps):
-        step()
-        log("  step %d enqueued" % i)
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
+    with SmiWatch(not args.no_gpu_state) as watch:
+        wall0 = time.perf_counter()
+        t_start.record()
+        for i in range(args.steps):
+            step()
+            log("  step %d enqueued" % i)
+        t_end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    state_after = None if args.no_gpu_state else gpu_state()
+    state_after = None if args.no_gpu_state else smi_sample()
 
     per = {}
     for name, t in timers.items():
@@ -474,7 +513,7 @@ def run(args):
         "config": {"workload": desc, "frames": N, "tokens_per_frame": L, "tokens": T,
                    "heads": H, "head_dim": HEAD_DIM},
         "roofline": roofline, "modes": per, "wall_s_timed": wall,
-        "gpu_state": {"before": state_before, "after": state_after},
+        "gpu_state": {"before": state_before, "during": watch.summary(), "after": state_after},
     }
     result.update(extra)
     if not args.no_cpu_baseline:
@@ -509,7 +548,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gpu-state", action="store_true",
-                    help="skip the rocm-smi clock query (for runs under a profiler)")
+                    help="skip the amd-smi power and clock samples (for runs under a profiler)")
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
