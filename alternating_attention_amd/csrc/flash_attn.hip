@@ -198,63 +198,6 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
     mset[qb] = false;
   }
 
-  if constexpr (KR == KeyRange::kSga) {
-    // Diagonal and mean columns start the shared softmax of each query.
-    const uint16_t* kf = (const uint16_t*)p.k_full;
-    const uint16_t* vf = (const uint16_t*)p.v_full;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int64_t row = min(tr.q_begin + wave * kQPerWave + qb * 32 + l32, tr.q_end - 1);
-      const bool diag = p.use_diag && !sga_kept(p.grid, p.row0 + row);
-      const uint16_t* qs = qg + ((size_t)row * H + head) * 64 + 8 * hf;
-      const uint16_t* ks = kf + ((size_t)row * H + head) * 64 + 8 * hf;
-      const float* kms = p.kmean + head * 64 + 8 * hf;
-      float dk = 0.f, dm = 0.f;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const u32x4 wq = *(const u32x4*)(qs + 16 * c);
-        const u32x4 wk = *(const u32x4*)(ks + 16 * c);
-        const f32x4 m0 = *(const f32x4*)(kms + 16 * c);
-        const f32x4 m1 = *(const f32x4*)(kms + 16 * c + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float qa = bf16_lo(wq[e]), qb2 = bf16_hi(wq[e]);
-          dk += qa * bf16_lo(wk[e]) + qb2 * bf16_hi(wk[e]);
-          const float ma = e < 2 ? m0[2 * e] : m1[2 * e - 4];
-          const float mb = e < 2 ? m0[2 * e + 1] : m1[2 * e - 3];
-          dm += qa * ma + qb2 * mb;
-        }
-      }
-      dk += __shfl_xor(dk, 32);
-      dm += __shfl_xor(dm, 32);
-      const float zd = dk * qscale;
-      const float zm = dm * qscale + p.log_ndrop * kLog2e;
-      if (diag || p.use_mean) {
-        float m0v = diag ? zd : zm;
-        if (diag && p.use_mean) m0v = fmaxf(zd, zm);
-        const float wd = diag ? exp2f(zd - m0v) : 0.f;
-        const float wm = p.use_mean ? exp2f(zm - m0v) : 0.f;
-        m[qb] = m0v;
-        mset[qb] = true;
-        lsum[qb] = hf == 0 ? wd + wm : 0.f;
-        const uint16_t* vs = vf + ((size_t)row * H + head) * 64;
-        const float* vms = p.vmean + head * 64;
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int d0 = 32 * db + 8 * g + 4 * hf;
-            const u32x2 wv = *(const u32x2*)(vs + d0);
-            const f32x4 mv = *(const f32x4*)(vms + d0);
-            o[qb][db][4 * g + 0] = wd * bf16_lo(wv[0]) + wm * mv[0];
-            o[qb][db][4 * g + 1] = wd * bf16_hi(wv[0]) + wm * mv[1];
-            o[qb][db][4 * g + 2] = wd * bf16_lo(wv[1]) + wm * mv[2];
-            o[qb][db][4 * g + 3] = wd * bf16_hi(wv[1]) + wm * mv[3];
-          }
-      }
-    }
-  }
-
   // ---- DMA plan: wave w issues the tile's 1 KB instructions w, w+8, ...
   // (0..17: K, 18..37: V).  A lane's granule: key offset within the tile and
   // byte offset within the row.
@@ -598,13 +541,76 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
   }
   pv(st, 3, Pb);  // drain
 
+  // This wave's first query row, recomputed here: the value from the Q load
+  // would otherwise be kept, in registers or scratch, across the loop.
+  int64_t row0 = tr.q_begin + wave * kQPerWave + l32;
+  asm volatile("" : "+v"(row0));
+
+  if constexpr (KR == KeyRange::kSga) {
+    // The diagonal and mean columns join each query's shared softmax here,
+    // merged into (m, l, O) after the compacted keys (the softmax sums do not
+    // depend on the column order).
+    const uint16_t* kf = (const uint16_t*)p.k_full;
+    const uint16_t* vf = (const uint16_t*)p.v_full;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int64_t row = min(row0 + qb * 32, tr.q_end - 1);
+      const bool diag = p.use_diag && !sga_kept(p.grid, p.row0 + row);
+      const uint16_t* ks = kf + ((size_t)row * H + head) * 64 + 8 * hf;
+      const float* kms = p.kmean + head * 64 + 8 * hf;
+      float dk = 0.f, dm = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x4 wq = __builtin_bit_cast(u32x4, qreg[qb][c]);  // dims 16c + 8hf + [0, 8)
+        const u32x4 wk = *(const u32x4*)(ks + 16 * c);
+        const f32x4 m0 = *(const f32x4*)(kms + 16 * c);
+        const f32x4 m1 = *(const f32x4*)(kms + 16 * c + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float qa = bf16_lo(wq[e]), qb2 = bf16_hi(wq[e]);
+          dk += qa * bf16_lo(wk[e]) + qb2 * bf16_hi(wk[e]);
+          const float ma = e < 2 ? m0[2 * e] : m1[2 * e - 4];
+          const float mb = e < 2 ? m0[2 * e + 1] : m1[2 * e - 3];
+          dm += qa * ma + qb2 * mb;
+        }
+      }
+      dk += __shfl_xor(dk, 32);
+      dm += __shfl_xor(dm, 32);
+      const float zd = dk * qscale;
+      const float zm = dm * qscale + p.log_ndrop * kLog2e;
+      if (diag || p.use_mean) {
+        float mn = mset[qb] ? m[qb] : -INFINITY;
+        if (diag) mn = fmaxf(mn, zd);
+        if (p.use_mean) mn = fmaxf(mn, zm);
+        const float f = mset[qb] ? exp2f(m[qb] - mn) : 0.f;
+        const float wd = diag ? exp2f(zd - mn) : 0.f;
+        const float wm = p.use_mean ? exp2f(zm - mn) : 0.f;
+        lsum[qb] = lsum[qb] * f + (hf == 0 ? wd + wm : 0.f);
+        const uint16_t* vs = vf + ((size_t)row * H + head) * 64;
+        const float* vms = p.vmean + head * 64;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d0 = 32 * db + 8 * g + 4 * hf;
+            const u32x2 wv = *(const u32x2*)(vs + d0);
+            const f32x4 mv = *(const f32x4*)(vms + d0);
+            o[qb][db][4 * g + 0] = o[qb][db][4 * g + 0] * f + wd * bf16_lo(wv[0]) + wm * mv[0];
+            o[qb][db][4 * g + 1] = o[qb][db][4 * g + 1] * f + wd * bf16_hi(wv[0]) + wm * mv[1];
+            o[qb][db][4 * g + 2] = o[qb][db][4 * g + 2] * f + wd * bf16_lo(wv[1]) + wm * mv[2];
+            o[qb][db][4 * g + 3] = o[qb][db][4 * g + 3] * f + wd * bf16_hi(wv[1]) + wm * mv[3];
+          }
+      }
+    }
+  }
+
   // ---- normalise and store O (bf16, RNE)
   uint16_t* __restrict__ og = (uint16_t*)p.o;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float l = lsum[qb] + __shfl_xor(lsum[qb], 32);
     const float inv = 1.f / l;
-    const int64_t row = tr.q_begin + wave * kQPerWave + qb * 32 + l32;
+    const int64_t row = row0 + qb * 32;
     if (row < tr.q_end) {
       uint16_t* dst = og + ((size_t)row * H + head) * 64;
 #pragma unroll

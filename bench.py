@@ -558,7 +558,7 @@ def main():
     if args.copy_probe:
         copy_probe()
         return
-    defaults = {"n100": (10, 2), "n300": (3, 1), "n800": (1, 1), "n800reg": (2, 1),
+    defaults = {"n100": (30, 20), "n300": (3, 1), "n800": (1, 1), "n800reg": (2, 1),
                 "shard8": (2, 1), "sweep": (2, 1)}[args.workload]
     args.steps = args.steps if args.steps is not None else defaults[0]
     args.warmup = args.warmup if args.warmup is not None else defaults[1]
