@@ -7,8 +7,9 @@ Bars (from the arithmetic the kernels use):
 * SGA keep_idx / keep_mask: bit-exact; kmean / vmean (fp32 sums): within
   1e-5 of the mean absolute dropped value, in absolute terms.
 Small cases compare every output; the full-size workloads (100, 300 and 800
-frames of 37x37+5 tokens, 16 heads) compare seeded sampled rows, which the
-oracle computes one by one.  The same bars apply to register attention, the
+frames of 37x37+5 tokens, 16 heads, and the largest shape the ABI accepts,
+1,526 frames) compare seeded sampled rows, which the oracle computes one by
+one.  The same bars apply to register attention, the
 unit-weight mean column and the row-range calls (whose rows are also
 compared with the same rows of the full call).
 """
@@ -257,6 +258,29 @@ def test_n800_full_size_frame_sga(vga):
     rows = _rows_with_tail(frames.tokens, 32, 44, frames.tokens_per_frame)
     run_and_compare(vga, frames, q, k, v, ["frame", "register"], [vga.Sga(3, 3, 1, 1)],
                     rows=rows, tag="N=800")
+
+
+def test_max_size_bf16(vga):
+    # the largest shape the ABI accepts at 16 heads: T*H*64 < 2^31 elements
+    # per tensor, 1,526 frames of 37x37+5 (T = 2,096,724; 4.3 GB per tensor)
+    L, H = 37 * 37 + 5, 16
+    N = (2 ** 31 // (H * 64) - 1) // L
+    assert N * L * H * 64 < 2 ** 31 <= (N + 1) * L * H * 64
+    frames = vga.Frames(N, 37, 37, 5, H)
+    q, k, v = vga_inputs.feature_field_qkv(N, 37, 37, 5, H, 64, seed=6, device="cuda")
+    T = frames.tokens
+    rows = _rows_with_tail(T, 16, 47, L)
+    run_and_compare(vga, frames, q, k, v, ["frame", "register"], [vga.Sga(3, 3, 1, 1)],
+                    rows=rows, tag="max")
+    # exact global attention for the last 700 query rows against all T keys
+    r0 = T - 700
+    say("case max global rows [%d, %d)" % (r0, T))
+    out = vga.global_attn_rows(q[r0:].contiguous(), k, v, frames, r0)
+    torch.cuda.synchronize()
+    sel = np.unique(np.concatenate([seeded_rows(700, 6, 48) + r0, [r0, T - 1]]))
+    ref = oracle.attention(oracle.MODE_GLOBAL, host(q), host(k), host(v), N, L, 37, 37, 0.125,
+                           rows=sel)
+    check(host(out[torch.from_numpy(sel - r0).cuda()]), ref, "bf16", "max global rows")
 
 
 # ------------------------------------------------------------ row-range calls
