@@ -6,19 +6,20 @@
 //   kFrame  -- the keys of a query are the L tokens of its own frame;
 //   kGlobal -- the keys are all T tokens; the T x T score matrix only ever
 //              exists one 32-key sub-tile at a time in registers;
-//   kSga    -- the keys are the compacted kept rows (Kc, Vc), and the
-//              softmax state of each query starts from its diagonal column
-//              (own token, when dropped) and the mean column (count-weighted
-//              or unit weight), so the three parts share one softmax.
+//   kSga    -- the keys are the compacted kept rows (Kc, Vc); after the
+//              key loop each query's diagonal column (own token, when
+//              dropped) and the mean column (count-weighted or unit weight)
+//              are merged into its softmax state, so the three parts share
+//              one softmax.
 //
 // bf16 path (MFMA).  A workgroup of 8 waves (two per SIMD) owns 512 queries
 // of one head; each wave owns 64 queries as two 32-query blocks.  Scores are
 // computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: keys
 // index the accumulator rows and queries its columns, so every lane holds
-// 16 scores of ONE query.  Row statistics therefore stay in the lane (plus its partner
-// lane l^32); the probabilities P^T feed O^T = V^T P^T directly as the B
-// operand without touching LDS.  K rows are stored in LDS in a permuted
-// order (bits 2 and 3 of the row index swapped) so that accumulator
+// 16 scores of ONE query.  Row statistics therefore stay in the lane (plus
+// its partner lane l^32); the probabilities P^T feed O^T = V^T P^T directly
+// as the B operand without touching LDS.  K rows are stored in LDS in a
+// permuted order (bits 2 and 3 of the row index swapped) so that accumulator
 // register r of lane half h holds key 16*(r/8) + 8*h + r%8 -- exactly the
 // B-operand k-slot order of the PV product.  V stays in its natural layout;
 // the PV A operand (V^T) comes from ds_read_b64_tr_b16 transposed reads.
