@@ -64,7 +64,7 @@ typedef enum {
   VGA_ERR_ALIGN = 5,       /* a device pointer is not 16-byte aligned       */
   VGA_ERR_ALIAS = 6,       /* O overlaps an input or the workspace          */
   VGA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than required       */
-  VGA_ERR_UNSUPPORTED = 8, /* head_dim != 64                                */
+  VGA_ERR_UNSUPPORTED = 8, /* head_dim != 64, or more heads than supported */
   VGA_ERR_HIP = 9          /* the HIP runtime reported an error             */
 } vga_status;
 
@@ -76,7 +76,8 @@ typedef struct {
   int32_t tokens_per_frame; /* L; must equal grid_h*grid_w + num_special     */
   int32_t grid_h, grid_w;   /* patch grid, e.g. 37 x 37 for 518px / 14px    */
   int32_t num_special;      /* S >= 0, stored after the patches of a frame   */
-  int32_t num_heads;        /* H >= 1                                        */
+  int32_t num_heads;        /* 1 <= H <= 64 (bf16) or 32 (fp32), else      *
+                             * VGA_ERR_UNSUPPORTED                          */
   int32_t head_dim;         /* D; must be 64                                 */
   int32_t dtype;            /* vga_dtype of Q, K, V and O                    */
   float scale;              /* softmax scale; <= 0 selects 1/sqrt(head_dim)  */

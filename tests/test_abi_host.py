@@ -83,6 +83,9 @@ def test_validation_statuses(vga):
     # too large: T*H*64 >= 2^31
     big = vga.Frames(num_frames=20000, grid_h=37, grid_w=37, num_special=5, num_heads=16)
     assert _call_global(vga, big.c(vga.VGA_BF16)) == 2
+    # head counts above the supported maximum: 64 in bf16, 32 in fp32
+    assert _call_global(vga, _frames(vga, num_heads=65).c(vga.VGA_BF16)) == 8
+    assert _call_global(vga, _frames(vga, num_heads=33).c(vga.VGA_F32)) == 8
     # frame attention shares the checks
     assert vga.lib.vga_frame_attn(ctypes.byref(ok), None, FAKE, FAKE, FAKE, None) == 1
 

@@ -169,6 +169,23 @@ def test_small_shapes(vga, shape, dt):
                     tag="%s-%s" % (shape, dt))
 
 
+@pytest.mark.parametrize("dt,H", [("bf16", 64), ("f32", 32)])
+def test_most_heads(vga, dt, H):
+    # the largest head counts the ABI accepts (64 in bf16, 32 in fp32): the
+    # gather then moves the widest rows, 1,024 chunks of 16 bytes per token
+    frames = vga.Frames(3, 6, 7, 2, H)
+    q, k, v = to_dev(tiny_qkv(frames.tokens, H, 64, seed=77),
+                     torch.float32 if dt == "f32" else torch.bfloat16)
+    run_and_compare(vga, frames, q, k, v, ["frame", "global", "register"],
+                    [vga.Sga(2, 2, 0, 0, True, True), vga.Sga(3, 2, 1, 1, True, 2)],
+                    tag="H=%d-%s" % (H, dt))
+    with pytest.raises(vga.VgaError) as ei:
+        more = vga.Frames(3, 6, 7, 2, H + 1)
+        x = torch.zeros(more.tokens, H + 1, 64, device="cuda", dtype=q.dtype)
+        vga.global_attn(x, x, x, more)
+    assert ei.value.status == 8
+
+
 def test_sga_flag_combinations_bf16(vga):
     frames = vga.Frames(3, 9, 8, 2, 2)
     q, k, v = to_dev(tiny_qkv(frames.tokens, 2, 64, seed=7), torch.bfloat16)
