@@ -42,6 +42,9 @@
  *    overlap Q, K, V or the workspace; each array at most 2^31 elements.
  *  - Thread safety: all calls are stateless and may run concurrently on
  *    different streams.
+ *  - Graph capture: a call enqueues kernel launches only (no allocation, no
+ *    memset, no host synchronisation without VGA_DEBUG_SYNC), so it may be
+ *    captured into a HIP graph; a replay recomputes the same result.
  */
 #ifndef VGA_H
 #define VGA_H

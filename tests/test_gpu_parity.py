@@ -221,6 +221,67 @@ def test_deterministic(vga):
     assert torch.equal(va["kmean"], vb["kmean"]) and torch.equal(va["vmean"], vb["vmean"])
 
 
+def test_graph_replay(vga):
+    # the calls enqueue kernels only (no memset, no allocation, no host sync),
+    # so they can be captured in a graph: every replay, with eager work and
+    # synchronisation between replays, equals the eager result bit for bit
+    frames = vga.Frames(3, 9, 8, 2, 2)
+    q, k, v = to_dev(tiny_qkv(frames.tokens, 2, 64, seed=21), torch.bfloat16)
+    sga = vga.Sga(2, 2, 0, 0)
+    ref = {"global": vga.global_attn(q, k, v, frames).clone()}
+    o, ws = vga.sga_attn(q, k, v, frames, sga)
+    ref["sga"] = o.clone()
+    o, rws = vga.register_attn(q, k, v, frames)
+    ref["register"] = o.clone()
+    outs = {m: torch.empty_like(q) for m in ref}
+
+    def calls():
+        vga.global_attn(q, k, v, frames, out=outs["global"])
+        vga.sga_attn(q, k, v, frames, sga, out=outs["sga"], workspace=ws)
+        vga.register_attn(q, k, v, frames, out=outs["register"], workspace=rws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    for i in range(4):
+        for t in outs.values():
+            t.zero_()
+        ws.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for m in ref:
+            assert torch.equal(outs[m], ref[m]), (i, m)
+
+
+def test_concurrent_streams(vga):
+    # two problems in flight on two streams give the results they give alone
+    fa = vga.Frames(4, 10, 10, 3, 2)
+    fb = vga.Frames(2, 7, 9, 5, 3)
+    qa, ka, va = to_dev(tiny_qkv(fa.tokens, 2, 64, seed=31), torch.bfloat16)
+    qb, kb, vb = to_dev(tiny_qkv(fb.tokens, 3, 64, seed=32), torch.bfloat16)
+    sga = vga.Sga(2, 3, 1, 0)
+    alone_a = vga.global_attn(qa, ka, va, fa).clone()
+    alone_b = vga.sga_attn(qb, kb, vb, fb, sga)[0].clone()
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs_a, outs_b = [], []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            outs_a.append(vga.global_attn(qa, ka, va, fa))
+        with torch.cuda.stream(s2):
+            outs_b.append(vga.sga_attn(qb, kb, vb, fb, sga)[0])
+    torch.cuda.synchronize()
+    for a, b in zip(outs_a, outs_b):
+        assert torch.equal(a, alone_a) and torch.equal(b, alone_b)
+
+
 def test_python_errors(vga):
     frames = vga.Frames(1, 4, 4, 0, 1)
     q = torch.zeros(16, 1, 64, device="cuda", dtype=torch.bfloat16)
