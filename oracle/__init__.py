@@ -23,6 +23,9 @@ What is computed follows the pages:
 * "VGGT-Omega" notes, section 2 (Register Attention) and architecture section
   2.3: in a register-attention layer only the per-frame register and camera
   tokens exchange information across frames; image tokens stay in their frame.
+* The projections around an attention layer (QKV before, output after), which
+  the pages do not spell out, read as plain nn.Linear-style layers
+  y = x W^T + b (``linear``, ``qkv_proj``).
 """
 from __future__ import annotations
 
@@ -75,6 +78,10 @@ def _load():
     lib.vgao_schedule_register.argtypes = [i32, i32, i32, i32, vp]
     lib.vgao_max_threads.restype = i32
     lib.vgao_max_threads.argtypes = []
+    lib.vgao_linear.restype = ctypes.c_int
+    lib.vgao_linear.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, i32]
+    lib.vgao_qkv_proj.restype = ctypes.c_int
+    lib.vgao_qkv_proj.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, i32]
     _lib = lib
     return lib
 
@@ -148,6 +155,49 @@ def attention(mode, q, k, v, N, L, gh, gw, scale, sga=None, rows=None, threads=0
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return out
+
+
+def linear(x, w, b=None, threads=0):
+    """fp64 y = x W^T + b for x [M, K], w [N, K] (output feature n in row n)
+    and b [N] or None, all float32 or all bf16 bits: the projections around
+    an attention layer, read as plain nn.Linear-style layers."""
+    lib = _load()
+    xx, dt = _elements(x)
+    ww, dtw = _elements(w)
+    assert xx.ndim == 2 and ww.ndim == 2 and xx.shape[1] == ww.shape[1] and dt == dtw
+    bp = None
+    if b is not None:
+        bb, dtb = _elements(b)
+        assert dtb == dt and bb.shape == (ww.shape[0],)
+        bp = _ptr(bb)
+    M, K = xx.shape
+    N = ww.shape[0]
+    y = np.empty((M, N), dtype=np.float64)
+    if lib.vgao_linear(M, K, N, dt, _ptr(xx), _ptr(ww), bp, _ptr(y), threads) != 0:
+        raise ValueError("oracle rejected the arguments")
+    return y
+
+
+def qkv_proj(x, w, b, H, threads=0):
+    """(q, k, v), each fp64 [M, H, 64], of the QKV projection: y = x W^T + b
+    with x [M, 64H], w [3*64H, 64H] and b [3*64H] or None; output features
+    [0, C), [C, 2C) and [2C, 3C) (C = 64H) are q, k and v."""
+    lib = _load()
+    xx, dt = _elements(x)
+    ww, dtw = _elements(w)
+    C = 64 * H
+    assert xx.ndim == 2 and xx.shape[1] == C and ww.shape == (3 * C, C) and dt == dtw
+    bp = None
+    if b is not None:
+        bb, dtb = _elements(b)
+        assert dtb == dt and bb.shape == (3 * C,)
+        bp = _ptr(bb)
+    M = xx.shape[0]
+    q, k, v = (np.empty((M, H, 64), dtype=np.float64) for _ in range(3))
+    if lib.vgao_qkv_proj(M, H, dt, _ptr(xx), _ptr(ww), bp, _ptr(q), _ptr(k), _ptr(v),
+                         threads) != 0:
+        raise ValueError("oracle rejected the arguments")
+    return q, k, v
 
 
 def schedule(num_global, num_early, use_sga):

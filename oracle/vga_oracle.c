@@ -286,6 +286,54 @@ int vgao_schedule_register(int32_t num_global, int32_t num_early,
 }
 
 /* Number of threads the oracle runs with (for reporting). */
+/* The linear projections around an attention layer (the QKV projection
+ * before it and the output projection after it), read as the plain
+ * nn.Linear-style layer the pages leave open: y = x W^T + b with
+ *   x [M, K] (M tokens, K input features), w [N, K] row-major (row n holds
+ *   the weights of output feature n), b [N] or NULL (no bias),
+ * all of one dtype, and y [M, N] in fp64:
+ *   y[m][n] = sum_k x[m][k] * w[n][k] + b[n].                               */
+int vgao_linear(int64_t M, int32_t K, int32_t N, int32_t dtype, const void* x,
+                const void* w, const void* b, double* y, int32_t threads) {
+  if (M < 0 || K < 1 || N < 1 || !x || !w || !y) return -1;
+#ifdef _OPENMP
+  if (threads > 0) omp_set_num_threads(threads);
+#else
+  (void)threads;
+#endif
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; ++m) {
+    for (int32_t n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int32_t k = 0; k < K; ++k)
+        acc += elem(x, dtype, m * K + k) * elem(w, dtype, (int64_t)n * K + k);
+      y[m * N + n] = acc + (b ? elem(b, dtype, n) : 0.0);
+    }
+  }
+  return 0;
+}
+
+/* QKV projection of H heads of 64: the C = 64*H input features of each of
+ * the M tokens map to 3C outputs, y = x W^T + b with w [3C, C]; output
+ * features [0, C) are q, [C, 2C) are k and [2C, 3C) are v, each stored
+ * [M, H, 64] (feature c = 64*h + e of head h, dim e).                       */
+int vgao_qkv_proj(int64_t M, int32_t H, int32_t dtype, const void* x, const void* w,
+                  const void* b, double* q, double* k, double* v, int32_t threads) {
+  const int32_t C = 64 * H;
+  if (H < 1 || !q || !k || !v) return -1;
+  double* y = (double*)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1) * 3 * C);
+  if (!y) return -1;
+  int rc = vgao_linear(M, C, 3 * C, dtype, x, w, b, y, threads);
+  for (int64_t m = 0; rc == 0 && m < M; ++m)
+    for (int32_t c = 0; c < C; ++c) {
+      q[m * C + c] = y[m * 3 * C + c];
+      k[m * C + c] = y[m * 3 * C + C + c];
+      v[m * C + c] = y[m * 3 * C + 2 * C + c];
+    }
+  free(y);
+  return rc;
+}
+
 int32_t vgao_max_threads(void) {
 #ifdef _OPENMP
   return (int32_t)omp_get_max_threads();

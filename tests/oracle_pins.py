@@ -19,7 +19,9 @@ Pins (none re-types the oracle's formula or re-calls a routine it uses):
   dropped keys == global (exact count weighting); diagonal present once;
   permutation equivariance over frames; Jensen bound on the mean column;
   register attention with no special tokens == frame attention;
-* brute force -- the numpy matrix formulation (oracle/brute.py).
+* brute force -- the numpy matrix formulation (oracle/brute.py);
+* projections -- a hand-computed linear layer (W against W^T), torch's
+  linear (fp64), and the q/k/v column split with block-scaled identities.
 """
 from __future__ import annotations
 
@@ -437,6 +439,57 @@ def pin_schedule(orc):
     assert list(r) == [F] * 8 + [S_, S_, S_, R] * 4
     assert int((orc.schedule_register(24, 0, 4, False) == R).sum()) == 6
     assert list(orc.schedule_register(6, 2, 0, True)) == list(orc.schedule(6, 2, True))
+
+
+# ------------------------------------------------- projections around a layer
+def _bf16_bits(a):
+    """float32 values that bf16 holds exactly -> raw bf16 bits."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    bits = a.view(np.uint32)
+    assert np.all(bits & 0xFFFF == 0), "value not exact in bf16"
+    return (bits >> 16).astype(np.uint16)
+
+
+def pin_linear_worked_example(orc):
+    # hand-computed: y = x W^T + b with W's rows the output features
+    x = np.array([[1, 2, 3], [4, 5, 6]], np.float32)
+    w = np.array([[1, 0, -1], [2, 1, 0]], np.float32)
+    b = np.array([0.5, -1], np.float32)
+    assert np.array_equal(orc.linear(x, w, b), [[-1.5, 3.0], [-1.5, 12.0]])
+    # a square, non-symmetric W tells W from W^T
+    x = np.array([[1, 2]], np.float32)
+    w = np.array([[0, 1], [3, 0]], np.float32)
+    assert np.array_equal(orc.linear(x, w), [[2.0, 3.0]])
+    assert np.array_equal(orc.linear(_bf16_bits(x), _bf16_bits(w)), [[2.0, 3.0]])
+
+
+def pin_linear_vs_torch(orc):
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((7, 128)).astype(np.float32)
+    w = rng.standard_normal((96, 128)).astype(np.float32)
+    b = rng.standard_normal(96).astype(np.float32)
+    ref = torch.nn.functional.linear(torch.from_numpy(_f64(x)), torch.from_numpy(_f64(w)),
+                                     torch.from_numpy(_f64(b))).numpy()
+    assert np.max(np.abs(orc.linear(x, w, b) - ref)) < 1e-12
+    ref = torch.nn.functional.linear(torch.from_numpy(_f64(x)), torch.from_numpy(_f64(w))).numpy()
+    assert np.max(np.abs(orc.linear(x, w) - ref)) < 1e-12
+
+
+def pin_qkv_split(orc):
+    # W = [I; 2I; 3I] and b = [0; 1; 2] (per block) give q = x, k = 2x + 1,
+    # v = 3x + 2, each as [M, H, 64] with feature 64h + e in head h, dim e
+    H, M = 2, 5
+    C = 64 * H
+    rng = np.random.default_rng(6)
+    x = rng.integers(-8, 9, size=(M, C)).astype(np.float32)
+    eye = np.eye(C, dtype=np.float32)
+    w = np.concatenate([eye, 2 * eye, 3 * eye])
+    b = np.repeat(np.arange(3, dtype=np.float32), C)
+    for conv in (lambda a: a, _bf16_bits):
+        q, k, v = orc.qkv_proj(conv(x), conv(w), conv(b), H)
+        xr = x.reshape(M, H, 64)
+        assert np.array_equal(q, xr) and np.array_equal(k, 2 * xr + 1)
+        assert np.array_equal(v, 3 * xr + 2)
 
 
 ALL_PINS = [v for kname, v in sorted(globals().items()) if kname.startswith("pin_")]

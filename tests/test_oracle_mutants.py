@@ -45,6 +45,13 @@ MUTANTS = [
     ("mean_not_divided", "kmean[i] /= (double)nd;", ";"),
     ("schedule_off_by_one", "out[g] = g < num_early ?", "out[g] = g <= num_early ?"),
     ("mean_value_is_key", "acc[e] += w * vmean[h * d + e];", "acc[e] += w * kmean[h * d + e];"),
+    ("linear_weight_transposed", "elem(w, dtype, (int64_t)n * K + k)",
+     "elem(w, dtype, (int64_t)k * N + n)"),
+    ("linear_bias_dropped", "y[m * N + n] = acc + (b ? elem(b, dtype, n) : 0.0);",
+     "y[m * N + n] = acc;"),
+    ("linear_bias_by_row", "elem(b, dtype, n)", "elem(b, dtype, m % N)"),
+    ("qkv_k_v_swapped", "k[m * C + c] = y[m * 3 * C + C + c];",
+     "k[m * C + c] = y[m * 3 * C + 2 * C + c];"),
 ]
 
 
