@@ -13,6 +13,8 @@ C names without the ``vga_`` prefix:
 * ``register_workspace_layout(frames)`` -> vga_register_workspace_layout
 * ``frame_attn_rows / global_attn_rows / sga_attn_rows(q_rows, k, v, frames,
   row_begin, ...)`` -> the ``vga_*_attn_rows`` row-range calls
+* ``qkv_proj(x, w, b, frames)`` -> vga_qkv_proj (returns q, k, v)
+* ``out_proj(o, w, b, frames)`` -> vga_out_proj
 * ``layer_schedule(num_global, num_early, sga)`` -> vga_layer_schedule
 * ``layer_schedule_register(num_global, num_early, register_every, sga)``
   -> vga_layer_schedule_register
@@ -43,6 +45,7 @@ EXPORTS = ["vga_frame_attn", "vga_global_attn", "vga_sga_workspace_layout",
            "vga_sga_attn", "vga_register_workspace_layout", "vga_register_attn",
            "vga_layer_schedule", "vga_layer_schedule_register",
            "vga_frame_attn_rows", "vga_global_attn_rows", "vga_sga_attn_rows",
+           "vga_qkv_proj", "vga_out_proj",
            "vga_status_string", "vga_last_error", "vga_abi_version"]
 
 
@@ -160,6 +163,10 @@ def _load():
     lib.vga_sga_attn_rows.restype = ctypes.c_int
     lib.vga_sga_attn_rows.argtypes = [ctypes.POINTER(CFrames), ctypes.POINTER(CSga), i64, i64,
                                       vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.vga_qkv_proj.restype = ctypes.c_int
+    lib.vga_qkv_proj.argtypes = [ctypes.POINTER(CFrames), vp, vp, vp, vp, vp, vp, vp]
+    lib.vga_out_proj.restype = ctypes.c_int
+    lib.vga_out_proj.argtypes = [ctypes.POINTER(CFrames), vp, vp, vp, vp, vp]
     lib.vga_status_string.restype = ctypes.c_char_p
     lib.vga_status_string.argtypes = [ctypes.c_int]
     lib.vga_last_error.restype = ctypes.c_char_p
@@ -397,6 +404,56 @@ def layer_schedule_register(num_global: int, num_early: int, register_every: int
     _check(lib.vga_layer_schedule_register(num_global, num_early, register_every,
                                            ctypes.byref(cs) if cs is not None else None, arr))
     return [(arr[i].mode, arr[i].sga) for i in range(num_global)]
+
+
+def _prepare_linear(x, w, b, frames: Frames, n_out: int):
+    C = frames.num_heads * frames.head_dim
+    for name, t, shape in (("x", x, (frames.tokens, C)), ("w", w, (n_out * C, C))):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous GPU tensor" % name)
+        if t.dtype != x.dtype or t.device != x.device:
+            raise ValueError("x and w must share dtype and device")
+        if t.numel() != shape[0] * shape[1]:
+            raise ValueError("%s must hold %d x %d elements" % (name, shape[0], shape[1]))
+    if b is not None and (not b.is_cuda or not b.is_contiguous() or b.dtype != x.dtype
+                          or b.numel() != n_out * C):
+        raise ValueError("b must be a contiguous GPU tensor of %d elements like x" % (n_out * C))
+    return C
+
+
+def qkv_proj(x, w, b, frames: Frames, out=None):
+    """QKV projection y = x w^T + b: x [T, C] (C = 64 H), w [3C, C], b [3C]
+    or None.  Returns (q, k, v), each [T, H, 64] (out: a tuple of three such
+    tensors to write into)."""
+    import torch
+    _prepare_linear(x, w, b, frames, 3)
+    shape = (frames.tokens, frames.num_heads, frames.head_dim)
+    if out is None:
+        out = tuple(torch.empty(shape, dtype=x.dtype, device=x.device) for _ in range(3))
+    for t in out:
+        if tuple(t.shape) != shape or t.dtype != x.dtype or not t.is_contiguous():
+            raise ValueError("q, k, v outputs must be contiguous [T, H, 64] like x")
+    cf = frames.c(_dtype_code(x))
+    _check(lib.vga_qkv_proj(ctypes.byref(cf), x.data_ptr(), w.data_ptr(),
+                            None if b is None else b.data_ptr(), out[0].data_ptr(),
+                            out[1].data_ptr(), out[2].data_ptr(), _stream(x.device)))
+    return out
+
+
+def out_proj(o, w, b, frames: Frames, out=None):
+    """Output projection y = o w^T + b: o [T, H, 64] (read as [T, C]),
+    w [C, C], b [C] or None.  Returns y [T, C]."""
+    import torch
+    C = _prepare_linear(o, w, b, frames, 1)
+    if out is None:
+        out = torch.empty((frames.tokens, C), dtype=o.dtype, device=o.device)
+    elif out.numel() != frames.tokens * C or out.dtype != o.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [T, C] tensor like o")
+    cf = frames.c(_dtype_code(o))
+    _check(lib.vga_out_proj(ctypes.byref(cf), o.data_ptr(), w.data_ptr(),
+                            None if b is None else b.data_ptr(), out.data_ptr(),
+                            _stream(o.device)))
+    return out
 
 
 def attention(mode: int, q, k, v, frames: Frames, sga: Sga | None = None, out=None,

@@ -12,7 +12,8 @@ LIB = os.path.join(PKG, "libvga.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["vga_api.cpp", "flash_attn.hip", "sga_gather.hip", "register_rows.hip"]
+SOURCES = ["vga_api.cpp", "flash_attn.hip", "sga_gather.hip", "register_rows.hip",
+           "proj_gemm.hip"]
 
 # Packed fp32 VALU instructions stay disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -1,0 +1,230 @@
+// proj_gemm.hip -- the linear projections around an attention layer for
+// gfx950 (MI355X): the QKV projection that produces Q, K, V and the output
+// projection after attention ("VGGT CVPR25 Best Paper" notes, section
+// "Alternating-Attention": each frame and global block is a self-attention
+// layer over the tokens; the pages leave the projections themselves open,
+// read here as nn.Linear-style layers).
+//
+//   Y[m][n] = sum_k X[m][k] * W[n][k] + b[n]
+//
+// X is [M, K] (M tokens, K = 64*H features), W is [N, K] row-major (row n
+// holds output feature n), b is [N] or absent.  The output columns go to up
+// to three [M, C] tensors: column n lands in tensor n / C at column n % C
+// (the QKV projection writes q, k and v; the output projection one tensor).
+//
+// bf16 path (MFMA).  A workgroup of 8 waves owns a 256 (tokens) x 256
+// (features) output tile and walks K in 64-wide steps through two LDS
+// stages, filled by global_load_lds_dwordx4 while the other stage is
+// computed.  The product is taken transposed, Y^T = W X^T, with
+// v_mfma_f32_32x32x16_bf16: both operands are then rows with K contiguous,
+// read from LDS with one pattern, and each lane ends with 16 features of one
+// token.  Each wave owns 128 features x 64 tokens (8 accumulators).  The
+// tile's bias is read into LDS once; the epilogue adds it in fp32, rounds
+// to bf16 (RNE), stages the tile in LDS and writes whole rows with 16-byte
+// stores.
+//
+// fp32 path: one thread per output, fp32 dot products in K order.
+#include <stdint.h>
+
+#include "vga_internal.h"
+
+namespace vga {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+constexpr int kThreads = 512;     // 8 waves
+constexpr int kBM = 256;          // tokens per tile
+constexpr int kBN = 256;          // output features per tile
+constexpr int kBK = 64;           // K per stage
+constexpr int kRow = 144;         // LDS bytes per row of 64 bf16 (128) + pad
+constexpr int kOpTile = 256 * kRow;              // 36864: one operand
+constexpr int kStage = 2 * kOpTile;              // 73728: W tile, then X tile
+constexpr int kGranules = 2 * 256 * 9;           // 16-byte granules per stage
+constexpr int kDmaPerWave = kGranules / 64 / 8;  // 9
+constexpr int kOutRow = 2 * kBN + 16;            // LDS bytes per staged output row
+static_assert(kGranules % 512 == 0, "DMA granules must split evenly over the waves");
+static_assert(kBM * kOutRow <= 2 * kStage, "the output tile must fit the LDS stages");
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2 p;
+  p[0] = (__bf16)lo;
+  p[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+__global__ void __launch_bounds__(kThreads, 1) linear_bf16_kernel(LinearParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[2][kStage];
+  __shared__ __attribute__((aligned(16))) uint16_t bias_s[kBN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const uint32_t n_tiles = (uint32_t)((p.N + kBN - 1) / kBN);
+  // Workgroup b runs on XCD b mod 8; each XCD takes one contiguous range of
+  // tiles, so the feature tiles of a token tile share its X rows in that
+  // XCD's L2.
+  const uint32_t nb = gridDim.x, x8 = blockIdx.x % 8u, per = nb / 8u, rem = nb % 8u;
+  const uint32_t bl = x8 * per + min(x8, rem) + blockIdx.x / 8u;
+  const int64_t m0 = (int64_t)(bl / n_tiles) * kBM;
+  const int64_t n0 = (int64_t)(bl % n_tiles) * kBN;
+  const int64_t K = p.K;
+  const int nk = (int)(K / kBK);
+
+  // DMA plan: granule i of a stage (i = 64 * (8 * s + wave) + lane) is
+  // operand i / 2304 (0: W, 1: X), row (i % 2304) / 9, 16-byte column
+  // (i % 9); column 8 is the row padding and loads column 0 again.  Rows
+  // past the matrix load its last row (their results are never stored).
+  // One instruction fills 1 KB of LDS: granules 64*j .. 64*j + 63 of the
+  // stage, lane by lane, so the LDS offset of granule i is 16*i and only the
+  // global address depends on the lane.
+  const char* src_base[kDmaPerWave];
+#pragma unroll
+  for (int s = 0; s < kDmaPerWave; ++s) {
+    const int i = 64 * (8 * s + wave) + lane;
+    const int op = i / 2304, r = (i % 2304) / 9, g = i % 9;
+    const int64_t row = op == 0 ? min(n0 + r, p.N - 1) : min(m0 + r, p.M - 1);
+    const char* base = op == 0 ? (const char*)p.w : (const char*)p.x;
+    src_base[s] = base + row * K * 2 + (g < 8 ? g * 16 : 0);
+  }
+  auto issue = [&](int kstep, int stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < kDmaPerWave; ++s) {
+      const char* src = src_base[s] + (int64_t)kstep * kBK * 2;
+      // Issued from asm, as in the attention kernel: the compiler's wait
+      // model would otherwise hold every later LDS read until this DMA
+      // lands.  Completion is awaited before each barrier.  The instruction
+      // writes LDS only and has no destination registers.
+      const uint32_t ldsa = __builtin_amdgcn_readfirstlane(
+          (uint32_t)(uintptr_t)&lds[stage][1024 * (8 * s + wave)]);
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                   :
+                   : "v"(src), "s"(ldsa)
+                   : "memory", "m0");
+    }
+  };
+
+  // operand reads: A = W rows (features), B = X rows (tokens), each lane
+  // row l32 of a 32-row block at k = 8*hf + [0, 8) of the 16-wide k step
+  const int wn = (wave & 1) * 128;   // this wave's features within the tile
+  const int wm = (wave >> 1) * 64;   // this wave's tokens within the tile
+  const int a_off = (wn + l32) * kRow + hf * 16;
+  const int b_off = kOpTile + (wm + l32) * kRow + hf * 16;
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    acc[nb][0] = 0.f;
+    acc[nb][1] = 0.f;
+  }
+
+  issue(0, 0);
+  // this tile's bias (zero past N or without a bias), read once
+  if (tid < kBN / 8) {
+    u32x4 bw = {0u, 0u, 0u, 0u};
+    const int64_t n = n0 + 8 * tid;
+    if (p.b && n < p.N) bw = *(const u32x4*)((const uint16_t*)p.b + n);
+    *(__attribute__((address_space(3))) u32x4*)&bias_s[8 * tid] = bw;
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  for (int s = 0; s < nk; ++s) {
+    const int st = s & 1;
+    if (s + 1 < nk) issue(s + 1, st ^ 1);  // its stage was last read in step s-1
+    const char* base = &lds[st][0];
+    bf16x8 a[2][4], b[2][2];
+    auto load = [&](int c, int buf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        a[buf][nb] = __builtin_bit_cast(
+            bf16x8, *(const lds_u32x4*)(base + a_off + nb * 32 * kRow + c * 32));
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        b[buf][mb] = __builtin_bit_cast(
+            bf16x8, *(const lds_u32x4*)(base + b_off + mb * 32 * kRow + c * 32));
+    };
+    load(0, 0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (c + 1 < 4) load(c + 1, (c + 1) & 1);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c & 1][nb], b[c & 1][mb],
+                                                                acc[nb][mb], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // the next stage has landed
+    __syncthreads();                     // and every wave is done with this one
+  }
+
+  // ---- epilogue: bias, bf16, staged in LDS as [token][feature] rows
+  char* out_tile = &lds[0][0];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int m = wm + 32 * mb + l32;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = wn + 32 * nb + 8 * g + 4 * hf;  // 4 consecutive features
+        const u32x2 bb = *(const __attribute__((address_space(3))) u32x2*)&bias_s[n];
+        const float bias[4] = {__uint_as_float(bb[0] << 16), __uint_as_float(bb[0] & 0xffff0000u),
+                               __uint_as_float(bb[1] << 16), __uint_as_float(bb[1] & 0xffff0000u)};
+        u32x2 w2;
+        w2[0] = pack_bf16(acc[nb][mb][4 * g + 0] + bias[0], acc[nb][mb][4 * g + 1] + bias[1]);
+        w2[1] = pack_bf16(acc[nb][mb][4 * g + 2] + bias[2], acc[nb][mb][4 * g + 3] + bias[3]);
+        *(__attribute__((address_space(3))) u32x2*)(out_tile + m * kOutRow + n * 2) = w2;
+      }
+    }
+  __syncthreads();
+  // 256 rows x 32 granules of 16 bytes; granule (row, j) holds features
+  // n0 + 8j .. n0 + 8j + 7 of token m0 + row
+#pragma unroll 4
+  for (int i = tid; i < kBM * (kBN / 8); i += kThreads) {
+    const int row = i >> 5, j = i & 31;
+    const int64_t m = m0 + row, n = n0 + 8 * j;
+    if (m >= p.M || n >= p.N) continue;
+    const int which = n >= 2 * p.C ? 2 : n >= p.C ? 1 : 0;
+    const int64_t col = n - which * p.C;
+    char* dst = (char*)p.y[which] + (m * p.C + col) * 2;
+    *(u32x4*)dst = *(const __attribute__((address_space(3))) u32x4*)(out_tile + row * kOutRow + j * 16);
+  }
+}
+
+__global__ void __launch_bounds__(256) linear_f32_kernel(LinearParams p) {
+  const int64_t total = p.M * p.N;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t m = i / p.N, n = i - m * p.N;
+    const float* xr = (const float*)p.x + m * p.K;
+    const float* wr = (const float*)p.w + n * p.K;
+    float acc = 0.f;
+    for (int64_t k = 0; k < p.K; ++k) acc = __builtin_fmaf(xr[k], wr[k], acc);
+    if (p.b) acc += ((const float*)p.b)[n];
+    const int which = n >= 2 * p.C ? 2 : n >= p.C ? 1 : 0;
+    ((float*)p.y[which])[m * p.C + (n - which * p.C)] = acc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_linear(bool bf16, const LinearParams& p, hipStream_t s) {
+  if (p.M <= 0) return hipSuccess;
+  if (bf16) {
+    const int64_t tiles = ((p.M + kBM - 1) / kBM) * ((p.N + kBN - 1) / kBN);
+    hipLaunchKernelGGL(linear_bf16_kernel, dim3((uint32_t)tiles), dim3(kThreads), 0, s, p);
+  } else {
+    int64_t blocks = (p.M * p.N + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(linear_f32_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace vga

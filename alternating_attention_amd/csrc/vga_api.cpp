@@ -342,9 +342,66 @@ vga_status schedule(int32_t num_global_layers, int32_t num_early_to_frame,
   return VGA_OK;
 }
 
+// y = x w^T + b with the columns split over outputs[0..n_out): shared by
+// the QKV projection (3 outputs of [T, C]) and the output projection (1).
+vga_status linear_run(const vga_frames* s, const void* x, const void* w, const void* b,
+                      void* const* outs, int n_out, void* stream, const char* what) {
+  Checked c;
+  vga_status st = check_shape(s, &c);
+  if (st != VGA_OK) return st;
+  if (!x || !w) return fail(VGA_ERR_NULL, "%s: x and w must be non-NULL", what);
+  for (int i = 0; i < n_out; ++i)
+    if (!outs[i]) return fail(VGA_ERR_NULL, "%s: outputs must be non-NULL", what);
+  const size_t es = elem_size(s->dtype);
+  const int64_t C = (int64_t)s->num_heads * vga::kHeadDim;
+  const size_t x_bytes = c.bytes;                     // [T, C]
+  const size_t w_bytes = (size_t)n_out * C * C * es;  // [n_out * C, C]
+  const size_t b_bytes = (size_t)n_out * C * es;
+  const void* aligned[2] = {x, w};
+  for (const void* p : aligned)
+    if ((uintptr_t)p % 16) return fail(VGA_ERR_ALIGN, "%s: %p is not 16-byte aligned", what, p);
+  for (int i = 0; i < n_out; ++i)
+    if ((uintptr_t)outs[i] % 16)
+      return fail(VGA_ERR_ALIGN, "%s: output %p is not 16-byte aligned", what, outs[i]);
+  if (b && (uintptr_t)b % es)
+    return fail(VGA_ERR_ALIGN, "%s: bias %p is not aligned to its element", what, b);
+  for (int i = 0; i < n_out; ++i) {
+    if (overlaps(outs[i], c.bytes, x, x_bytes) || overlaps(outs[i], c.bytes, w, w_bytes) ||
+        (b && overlaps(outs[i], c.bytes, b, b_bytes)))
+      return fail(VGA_ERR_ALIAS, "%s: an output overlaps an input", what);
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], c.bytes, outs[j], c.bytes))
+        return fail(VGA_ERR_ALIAS, "%s: two outputs overlap", what);
+  }
+  vga::LinearParams p;
+  memset(&p, 0, sizeof p);
+  p.x = x;
+  p.w = w;
+  p.b = b;
+  for (int i = 0; i < n_out; ++i) p.y[i] = outs[i];
+  p.M = c.T;
+  p.K = C;
+  p.N = n_out * C;
+  p.C = C;
+  hipStream_t hs = (hipStream_t)stream;
+  return finish(vga::launch_linear(s->dtype == VGA_BF16, p, hs), hs, what);
+}
+
 }  // namespace
 
 extern "C" {
+
+vga_status vga_qkv_proj(const vga_frames* shape, const void* x, const void* w_qkv,
+                        const void* b_qkv, void* q, void* k, void* v, void* stream) {
+  void* outs[3] = {q, k, v};
+  return linear_run(shape, x, w_qkv, b_qkv, outs, 3, stream, "vga_qkv_proj");
+}
+
+vga_status vga_out_proj(const vga_frames* shape, const void* o, const void* w_o,
+                        const void* b_o, void* y, void* stream) {
+  void* outs[1] = {y};
+  return linear_run(shape, o, w_o, b_o, outs, 1, stream, "vga_out_proj");
+}
 
 vga_status vga_frame_attn(const vga_frames* shape, const void* q, const void* k,
                           const void* v, void* o, void* stream) {

@@ -78,11 +78,26 @@ struct SpecialRowsParams {
   int32_t to_compact;
 };
 
+// Arguments of the projection kernels: Y = X W^T + b, X [M, K], W [N, K],
+// b [N] or NULL, Y columns split over up to three [M, C] tensors (column n
+// goes to y[n / C] at column n % C).
+struct LinearParams {
+  const void* x;
+  const void* w;
+  const void* b;
+  void* y[3];
+  int64_t M;
+  int64_t K;
+  int64_t N;
+  int64_t C;
+};
+
 // Launchers (return the HIP status of the launch).
 hipError_t launch_flash_bf16(KeyRange kr, const FlashParams& p, hipStream_t s);
 hipError_t launch_flash_f32(KeyRange kr, const FlashParams& p, hipStream_t s);
 hipError_t launch_sga_gather(bool bf16, const GatherParams& p, hipStream_t s);
 hipError_t launch_special_rows(const SpecialRowsParams& p, hipStream_t s);
+hipError_t launch_linear(bool bf16, const LinearParams& p, hipStream_t s);
 
 // Number of partial-sum blocks of the gather for T tokens.
 int32_t gather_blocks(int64_t T);

@@ -64,6 +64,11 @@ def flops_sga(T, num_kept, H, d=HEAD_DIM):
     return 4.0 * T * num_kept * d * H
 
 
+def flops_linear(T, c_in, c_out):
+    """y = x W^T + b for T tokens: 2*T*c_in*c_out (the bias is negligible)."""
+    return 2.0 * T * c_in * c_out
+
+
 def bytes_gather(T, num_kept, H, d=HEAD_DIM, esize=2):
     """Read K and V once, write the kept rows of both."""
     return 2.0 * T * H * d * esize + 2.0 * num_kept * H * d * esize
@@ -98,10 +103,13 @@ class Timer:
 
 
 def cpu_baseline(workload, frames, sga_list, modes, qkv_host, rows_count, seed=7,
-                 row_range=None):
+                 row_range=None, proj=None):
     """The fp64 oracle on a bounded sample: `rows_count` seeded query rows
     (all heads) of each mode of the step, extrapolated x (rows of the step) /
-    rows_count.  row_range: the step's query rows (default all T)."""
+    rows_count.  row_range: the step's query rows (default all T).  proj:
+    (x, w_qkv, b_qkv, w_o, b_o) host bits when every attention layer of the
+    step sits between a QKV and an output projection (their rows are timed
+    too)."""
     import oracle
     q, k, v = qkv_host
     T = frames.tokens
@@ -119,6 +127,12 @@ def cpu_baseline(workload, frames, sga_list, modes, qkv_host, rows_count, seed=7
                          dict(stride_h=p.stride_h, stride_w=p.stride_w, phase_h=p.phase_h,
                               phase_w=p.phase_w, diagonal=int(p.diagonal),
                               mean_fill=int(p.mean_fill)), rows=rows)
+    if proj is not None:
+        x, wqkv, bqkv, wo, bo = proj
+        xr = np.ascontiguousarray(x[rows])
+        for _ in list(modes) + list(sga_list):
+            oracle.qkv_proj(xr, wqkv, bqkv, frames.num_heads)
+            oracle.linear(xr, wo, bo)
     dt = time.perf_counter() - t0
     step_s = dt * (r1 - r0) / rows_count
     return {"value": (r1 - r0) / step_s, "unit": "tokens/s", "cores": oracle.max_threads(),
@@ -126,7 +140,9 @@ def cpu_baseline(workload, frames, sga_list, modes, qkv_host, rows_count, seed=7
             "sample": "%d seeded query rows x %d heads of each layer of the step (%s), "
                       "timed %.1f s, extrapolated x %d/%d" % (
                           rows_count, frames.num_heads,
-                          "+".join(list(modes) + ["sga"] * len(sga_list)), dt, r1 - r0,
+                          "+".join(list(modes) + ["sga"] * len(sga_list))
+                          + (", each with its QKV and output projections" if proj else ""),
+                          dt, r1 - r0,
                           rows_count),
             "seconds_per_step": step_s}
 
@@ -238,7 +254,7 @@ def run(args):
     import alternating_attention_amd as vga
     import vga_inputs
 
-    base = {"n800reg": "n800", "shard8": "n800", "sweep": "n300"}
+    base = {"n800reg": "n800", "shard8": "n800", "sweep": "n300", "block": "n100"}
     w = vga_inputs.WORKLOADS[base.get(args.workload, args.workload)]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -257,7 +273,28 @@ def run(args):
         with t:
             fn()
 
-    if args.workload == "n100":
+    if args.workload == "block":
+        C = H * HEAD_DIM
+        log("generating block inputs (token features and projection weights)")
+        x, wqkv, bqkv, wo, bo = vga_inputs.feature_field_block(
+            N, w.grid_h, w.grid_w, w.num_special, H, seed=w.seed + 10, device=dev)
+        qkv = tuple(torch.empty_like(q) for _ in range(3))
+        y = torch.empty((T, C), dtype=torch.bfloat16, device=dev)
+        desc = ("N=100 frames x 1374 tokens = 137,400 tokens, 16 heads x 64 (C = 1024), bf16; "
+                "step = a frame block and a global block, each the QKV projection "
+                "(y = x W^T + b, 1024 -> 3072), the attention layer and the output "
+                "projection (1024 -> 1024)")
+
+        def step():
+            for kind, fn in (("frame", vga.frame_attn), ("global", vga.global_attn)):
+                timed("qkv_" + kind, lambda: vga.qkv_proj(x, wqkv, bqkv, frames, qkv))
+                timed(kind, lambda fn=fn: fn(qkv[0], qkv[1], qkv[2], frames, out))
+                timed("out_" + kind, lambda: vga.out_proj(out, wo, bo, frames, y))
+        work = {"frame": flops_frame(N, L, H), "global": flops_global(T, H),
+                "qkv_frame": flops_linear(T, C, 3 * C), "qkv_global": flops_linear(T, C, 3 * C),
+                "out_frame": flops_linear(T, C, C), "out_global": flops_linear(T, C, C)}
+        dominant, modes, sgas = "global", ["frame", "global"], []
+    elif args.workload == "n100":
         sga = vga.Sga(2, 2, 0, 0, True, True)
         lay = vga.sga_workspace_layout(frames, sga)
         ws = torch.empty(int(lay.total), dtype=torch.uint8, device=dev)
@@ -499,9 +536,19 @@ def run(args):
     ach = flop_dom / (per[dominant]["ms_per_call"] * 1e-3) / 1e12
     kernel = {"global": "flash_bf16_kernel<kGlobal>", "sga": "flash_bf16_kernel<kSga>",
               "sga_2x2": "flash_bf16_kernel<kSga>"}[dominant]
+    if args.workload == "block":
+        bl = {}
+        for kind in ("frame", "global"):
+            parts = [per[n]["ms_per_call"] for n in ("qkv_" + kind, kind, "out_" + kind)]
+            bl[kind + "_block_ms"] = sum(parts)
+            bl[kind + "_projection_share"] = (parts[0] + parts[2]) / sum(parts)
+        extra_block = bl
+    else:
+        extra_block = None
     roofline = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / PEAK_BF16_TFLOPS,
-                "traffic": measured_traffic(kernel) if args.workload == "n100" else None,
+                "traffic": (measured_traffic(kernel) if args.workload in ("n100", "block")
+                            else None),
                 "kernel": kernel, "algorithmic_flops_per_launch": flop_dom}
 
     result = {
@@ -516,12 +563,18 @@ def run(args):
         "gpu_state": {"before": state_before, "during": watch.summary(), "after": state_after},
     }
     result.update(extra)
+    if extra_block:
+        result["blocks"] = extra_block
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, %d rows per layer)" % args.cpu_rows)
         qkv = (host_bits(q, torch), host_bits(k, torch), host_bits(v, torch))
+        proj = None
+        if args.workload == "block":
+            proj = tuple(host_bits(t, torch) for t in (x, wqkv, bqkv, wo, bo))
         result["cpu_baseline"] = cpu_baseline(
             w, frames, sgas, modes, qkv, args.cpu_rows,
-            row_range=(3 * T // 8, 4 * T // 8) if args.workload == "shard8" else None)
+            row_range=(3 * T // 8, 4 * T // 8) if args.workload == "shard8" else None,
+            proj=proj)
     return result
 
 
@@ -544,7 +597,7 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="n100",
-                    choices=["n100", "n300", "n800", "n800reg", "shard8", "sweep"])
+                    choices=["n100", "n300", "n800", "n800reg", "shard8", "sweep", "block"])
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gpu-state", action="store_true",
@@ -559,7 +612,7 @@ def main():
         copy_probe()
         return
     defaults = {"n100": (30, 20), "n300": (3, 1), "n800": (1, 1), "n800reg": (2, 1),
-                "shard8": (2, 1), "sweep": (2, 1)}[args.workload]
+                "shard8": (2, 1), "sweep": (2, 1), "block": (10, 5)}[args.workload]
     args.steps = args.steps if args.steps is not None else defaults[0]
     args.warmup = args.warmup if args.warmup is not None else defaults[1]
     res = run(args)

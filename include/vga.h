@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define VGA_ABI_VERSION 2
+#define VGA_ABI_VERSION 3
 
 typedef enum {
   VGA_OK = 0,
@@ -229,6 +229,32 @@ vga_status vga_sga_attn_rows(const vga_frames* shape, const vga_sga* sga, int64_
                              int64_t row_end, const void* q_rows, const void* k,
                              const void* v, void* o_rows, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* The projections around an attention layer ("VGGT CVPR25 Best Paper"
+ * notes, section "Alternating-Attention": the frame and global blocks are
+ * self-attention layers over the tokens).  The pages leave the projections
+ * open; they are taken as plain nn.Linear-style layers,
+ *   y[t][n] = sum_c x[t][c] * w[n][c] + b[n],
+ * with C = 64 * num_heads input features per token, all arrays of the
+ * shape's dtype (fp32 or bf16; accumulation in fp32).  No positional
+ * encoding is applied (the pages do not specify VGGT's).
+ *
+ * vga_qkv_proj: x [T, C] token features; w_qkv [3C, C] row-major (row n is
+ * output feature n); b_qkv [3C] or NULL for no bias.  Output features
+ * [0, C), [C, 2C) and [2C, 3C) are written to q, k and v, each [T, H, 64]
+ * (feature 64*h + e is head h, dim e) -- the layout the attention calls take.
+ *
+ * vga_out_proj: o [T, H, 64] (an attention output, read as [T, C]);
+ * w_o [C, C]; b_o [C] or NULL; y [T, C].
+ *
+ * x, w, q, k, v, o and y must be 16-byte aligned and the bias aligned to
+ * its element size; the outputs must not overlap an input or each other.
+ * Errors: VGA_ERR_NULL, VGA_ERR_SHAPE, VGA_ERR_DTYPE, VGA_ERR_ALIGN,
+ * VGA_ERR_ALIAS, VGA_ERR_UNSUPPORTED (shape checks), VGA_ERR_HIP. */
+vga_status vga_qkv_proj(const vga_frames* shape, const void* x, const void* w_qkv,
+                        const void* b_qkv, void* q, void* k, void* v, void* stream);
+vga_status vga_out_proj(const vga_frames* shape, const void* o, const void* w_o,
+                        const void* b_o, void* y, void* stream);
 
 const char* vga_status_string(vga_status status);
 const char* vga_last_error(void); /* thread-local detail of the last failure */

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(vga):
 
 
 def test_abi_version_and_strings(vga):
-    assert vga.abi_version() == 2
+    assert vga.abi_version() == 3
     for code, name in enumerate(vga.STATUS_NAMES):
         assert vga.status_string(code) == name
 
@@ -148,6 +148,35 @@ def test_rows_validation(vga):
     bad = vga.Sga(stride_h=0).c()
     assert vga.lib.vga_sga_attn_rows(ctypes.byref(cf), ctypes.byref(bad), 3, 3, None, None,
                                      None, None, None, 0, None) == 4
+
+
+def test_projection_validation(vga):
+    f = _frames(vga, num_heads=2)           # C = 128, T = 138
+    cf = f.c(vga.VGA_BF16)
+    X, W, B = FAKE, FAKE + 0x1000000, FAKE + 0x2000000
+    Q, K, V = FAKE + 0x3000000, FAKE + 0x4000000, FAKE + 0x5000000
+
+    def qkv(x=X, w=W, b=B, q=Q, k=K, v=V, shape=cf):
+        return vga.lib.vga_qkv_proj(ctypes.byref(shape), x, w, b, q, k, v, None)
+
+    def outp(o=X, w=W, b=B, y=Q):
+        return vga.lib.vga_out_proj(ctypes.byref(cf), o, w, b, y, None)
+
+    assert qkv(x=None) == 1 and qkv(w=None) == 1 and qkv(v=None) == 1
+    assert outp(y=None) == 1
+    assert vga.lib.vga_qkv_proj(None, X, W, B, Q, K, V, None) == 1
+    assert qkv(x=X + 8) == 5 and qkv(k=K + 4) == 5
+    assert qkv(b=B + 1) == 5                 # bias must be element-aligned
+    assert qkv(q=X + 256) == 6               # q overlaps x
+    assert qkv(k=W + 0x100) == 6             # k overlaps w
+    assert qkv(v=Q + 0x1000) == 6            # v overlaps q
+    assert qkv(q=B) == 6                     # q overlaps the bias
+    assert outp(y=X) == 6
+    bad = f.c(vga.VGA_BF16)
+    bad.dtype = 5
+    assert qkv(shape=bad) == 3
+    bad = f.c(vga.VGA_BF16, tokens_per_frame=70)
+    assert qkv(shape=bad) == 2
 
 
 def test_register_layout_and_validation(vga):

@@ -13,6 +13,7 @@ one.  The same bars apply to register attention, the
 unit-weight mean column and the row-range calls (whose rows are also
 compared with the same rows of the full call).
 """
+import math
 import sys
 
 import numpy as np
@@ -292,6 +293,56 @@ def test_python_errors(vga):
     with pytest.raises(vga.VgaError) as ei:
         vga.global_attn(q, q, q, frames, out=q)       # o aliases q
     assert ei.value.status == 6
+
+
+# --------------------------------------------- projections around a layer
+# Bars for y = x W^T + b (fp32 accumulation over K = 64 H terms): fp32 path
+# max-abs 1e-5; bf16 path |err| <= 2^-8 |y| + 2^-10 per element -- the RNE
+# rounding of y to bf16 (at most 2^-9 |y|) plus the fp32 accumulation.
+PROJ_SHAPES = [
+    # N, gh, gw, S, H -- ragged token counts; C = 128..1024; 3C not a
+    # multiple of the 256-wide feature tile for H = 2, 3
+    (3, 7, 9, 3, 2),
+    (5, 11, 13, 4, 3),
+    (2, 16, 16, 1, 4),
+    (1, 20, 20, 5, 16),
+]
+
+
+def check_linear(got, ref, dtype, what):
+    err = np.abs(as_f64(got) - ref)
+    say("  %s: max-abs %.3g (|y| max %.3g)" % (what, float(err.max()), float(np.abs(ref).max())))
+    if dtype == "f32":
+        assert float(err.max()) <= F32_MAX, what
+    else:
+        assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 2.0 ** -10), what
+
+
+@pytest.mark.parametrize("shape", PROJ_SHAPES, ids=lambda s: "N%d_%dx%d_S%d_H%d" % s)
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_projections(vga, shape, dt):
+    N, gh, gw, S, H = shape
+    frames = vga.Frames(N, gh, gw, S, H)
+    T, C = frames.tokens, 64 * H
+    rng = np.random.default_rng(500 + 7 * H + N)
+    x = rng.standard_normal((T, C)).astype(np.float32)
+    w = (rng.standard_normal((3 * C, C)) / math.sqrt(C)).astype(np.float32)
+    b = rng.standard_normal(3 * C).astype(np.float32)
+    wo = (rng.standard_normal((C, C)) / math.sqrt(C)).astype(np.float32)
+    bo = rng.standard_normal(C).astype(np.float32)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    xd, wd, bd, wod, bod = to_dev((x, w, b, wo, bo), tdt)
+    for bias in (True, False):
+        say("case proj-%s %s bias=%s" % (dt, shape, bias))
+        q, k, v = vga.qkv_proj(xd, wd, bd if bias else None, frames)
+        torch.cuda.synchronize()
+        rq, rk, rv = oracle.qkv_proj(host(xd), host(wd), host(bd) if bias else None, H)
+        for name, got, ref in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
+            check_linear(host(got), ref, dt, "qkv %s" % name)
+        y = vga.out_proj(q, wod, bod if bias else None, frames)
+        torch.cuda.synchronize()
+        ry = oracle.linear(host(q).reshape(T, C), host(wod), host(bod) if bias else None)
+        check_linear(host(y), ry, dt, "out")
 
 
 # ------------------------------------------- feature-field workloads (sampled)

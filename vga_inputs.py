@@ -18,6 +18,12 @@ Two recipes:
   W ~ N(0, 1/C) [C, C], C = H*64, computed in fp32 and rounded to bf16, viewed
   as [T, H, 64].  Draw order: F, shifts, specials, eps, Wq, Wk, Wv, all from
   one ``torch.Generator`` on the target device seeded with ``seed``.
+* ``feature_field_block`` -- the inputs of a whole attention block (the
+  projections around the attention): the same token features X (before any
+  projection) in bf16 [T, C], and the weights of the QKV projection
+  W_qkv ~ N(0, 1/C) [3C, C] with bias b_qkv ~ N(0, 0.1^2) [3C], and of the
+  output projection W_o ~ N(0, 1/C) [C, C] with b_o ~ N(0, 0.1^2) [C], drawn
+  after X in that order from the same generator.
 """
 from __future__ import annotations
 
@@ -99,6 +105,36 @@ def feature_field_qkv(N: int, gh: int, gw: int, S: int, H: int, d: int = 64,
         del w
     del x
     return tuple(out)
+
+
+def feature_field_block(N: int, gh: int, gw: int, S: int, H: int, seed: int = 1,
+                        device="cpu"):
+    """(x, w_qkv, b_qkv, w_o, b_o) in bf16: shifted-feature-field tokens
+    [N*L, 64H] and random projection weights (see the module docstring)."""
+    import torch
+
+    C = H * 64
+    L = gh * gw + S
+    T = N * L
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    field = torch.randn(gh + 16, gw + 16, C, generator=g, device=device)
+    shifts = torch.randint(-8, 9, (N, 2), generator=g, device=device).cpu()
+    specials = torch.randn(S, C, generator=g, device=device)
+    x = torch.randn(T, C, generator=g, device=device).mul_(0.1)
+    rows = torch.arange(gh, device=device).view(gh, 1) + 8
+    cols = torch.arange(gw, device=device).view(1, gw) + 8
+    xv = x.view(N, L, C)
+    for f in range(N):
+        dy, dx = int(shifts[f, 0]), int(shifts[f, 1])
+        xv[f, : gh * gw] += field[rows + dy, cols + dx].reshape(gh * gw, C)
+        xv[f, gh * gw:] += specials
+    bf = torch.bfloat16
+    w_qkv = torch.randn(3 * C, C, generator=g, device=device).mul_(C ** -0.5).to(bf)
+    b_qkv = torch.randn(3 * C, generator=g, device=device).mul_(0.1).to(bf)
+    w_o = torch.randn(C, C, generator=g, device=device).mul_(C ** -0.5).to(bf)
+    b_o = torch.randn(C, generator=g, device=device).mul_(0.1).to(bf)
+    return x.to(bf), w_qkv, b_qkv, w_o, b_o
 
 
 def seeded_rows(T: int, count: int, seed: int) -> np.ndarray:
