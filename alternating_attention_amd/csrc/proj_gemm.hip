@@ -15,13 +15,17 @@
 // bf16 path (MFMA).  A workgroup of 8 waves owns a 256 (tokens) x 256
 // (features) output tile and walks K in 64-wide steps through two LDS
 // stages, filled by global_load_lds_dwordx4 while the other stage is
-// computed.  The product is taken transposed, Y^T = W X^T, with
-// v_mfma_f32_32x32x16_bf16: both operands are then rows with K contiguous,
-// read from LDS with one pattern, and each lane ends with 16 features of one
-// token.  Each wave owns 128 features x 64 tokens (8 accumulators).  The
-// tile's bias is read into LDS once; the epilogue adds it in fp32, rounds
-// to bf16 (RNE), stages the tile in LDS and writes whole rows with 16-byte
-// stores.
+// computed.  A stage holds 256 W rows and 256 X rows of 128 bytes each,
+// their 16-byte granules permuted within the row (XOR swizzle) instead of
+// padded, so the DMA moves no padding.  The product is taken transposed,
+// Y^T = W X^T, with v_mfma_f32_32x32x16_bf16: both operands are then rows
+// with K contiguous, read from LDS with one pattern, and each lane ends with
+// 16 features of one token.  Each wave owns 128 features x 64 tokens (8
+// accumulators); the operand reads of the next 16-wide k step are pinned
+// between the MFMAs of the current one, so no MFMA waits on a read just
+// issued.  The tile's bias is read into LDS once; the epilogue adds it in
+// fp32, rounds to bf16 (RNE), stages the tile in LDS and writes whole rows
+// with 16-byte stores.
 //
 // fp32 path: one thread per output, fp32 dot products in K order.
 #include <stdint.h>
@@ -42,14 +46,17 @@ constexpr int kThreads = 512;     // 8 waves
 constexpr int kBM = 256;          // tokens per tile
 constexpr int kBN = 256;          // output features per tile
 constexpr int kBK = 64;           // K per stage
-constexpr int kRow = 144;         // LDS bytes per row of 64 bf16 (128) + pad
-constexpr int kOpTile = 256 * kRow;              // 36864: one operand
-constexpr int kStage = 2 * kOpTile;              // 73728: W tile, then X tile
-constexpr int kGranules = 2 * 256 * 9;           // 16-byte granules per stage
-constexpr int kDmaPerWave = kGranules / 64 / 8;  // 9
+constexpr int kRow = 128;         // LDS bytes per row of 64 bf16, 16-byte slots swizzled
+constexpr int kOpTile = 256 * kRow;              // 32768: one operand
+constexpr int kStage = 2 * kOpTile;              // 65536: W tile, then X tile
+constexpr int kDmaPerWave = kStage / 1024 / 8;   // 8
 constexpr int kOutRow = 2 * kBN + 16;            // LDS bytes per staged output row
-static_assert(kGranules % 512 == 0, "DMA granules must split evenly over the waves");
-static_assert(kBM * kOutRow <= 2 * kStage, "the output tile must fit the LDS stages");
+constexpr int kLds = kBM * kOutRow > 2 * kStage ? kBM * kOutRow : 2 * kStage;
+
+// Granule g (k = 8g .. 8g+7) of row r sits in slot g ^ swz(r): any 16
+// consecutive rows (two per 256-byte bank line) and any 8 consecutive rows
+// use distinct bank groups for one granule.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   bf16x2 p;
@@ -59,7 +66,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 }
 
 __global__ void __launch_bounds__(kThreads, 1) linear_bf16_kernel(LinearParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[2][kStage];
+  __shared__ __attribute__((aligned(16))) char lds[kLds];
   __shared__ __attribute__((aligned(16))) uint16_t bias_s[kBN];
 
   const int tid = threadIdx.x;
@@ -76,45 +83,57 @@ __global__ void __launch_bounds__(kThreads, 1) linear_bf16_kernel(LinearParams p
   const int64_t K = p.K;
   const int nk = (int)(K / kBK);
 
-  // DMA plan: granule i of a stage (i = 64 * (8 * s + wave) + lane) is
-  // operand i / 2304 (0: W, 1: X), row (i % 2304) / 9, 16-byte column
-  // (i % 9); column 8 is the row padding and loads column 0 again.  Rows
+  // DMA plan: instruction j = 8 * s + wave (s < 8) of a stage fills LDS
+  // bytes [1024 j, 1024 j + 1024), lane by lane: W rows for j < 32, X rows
+  // after.  Lane l writes slot l % 8 of row 8 (j % 32) + l / 8 of its
+  // operand, i.e. loads global granule (l % 8) ^ swz(row) of that row.  Rows
   // past the matrix load its last row (their results are never stored).
-  // One instruction fills 1 KB of LDS: granules 64*j .. 64*j + 63 of the
-  // stage, lane by lane, so the LDS offset of granule i is 16*i and only the
-  // global address depends on the lane.
+  // The base pointer of an instruction is wave-uniform and the lane only
+  // adds a 32-bit offset (every operand is below 4 GiB).
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t src_off[kDmaPerWave];
   const char* src_base[kDmaPerWave];
 #pragma unroll
   for (int s = 0; s < kDmaPerWave; ++s) {
-    const int i = 64 * (8 * s + wave) + lane;
-    const int op = i / 2304, r = (i % 2304) / 9, g = i % 9;
-    const int64_t row = op == 0 ? min(n0 + r, p.N - 1) : min(m0 + r, p.M - 1);
-    const char* base = op == 0 ? (const char*)p.w : (const char*)p.x;
-    src_base[s] = base + row * K * 2 + (g < 8 ? g * 16 : 0);
+    // a value in SGPRs: the DMA asm clobbers memory, so the kernel argument
+    // would otherwise be read again after every instruction
+    src_base[s] = s < 4 ? (const char*)p.w : (const char*)p.x;
+    asm volatile("" : "+s"(src_base[s]));
+    const int j = 8 * s + wave_u;
+    const int r = 8 * (j % 32) + lane / 8;      // row within the operand tile
+    const int g = (lane % 8) ^ swz(r & 31);
+    const int64_t row = s < 4 ? min(n0 + r, p.N - 1) : min(m0 + r, p.M - 1);
+    src_off[s] = (uint32_t)(row * K * 2 + g * 16);
   }
   auto issue = [&](int kstep, int stage) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < kDmaPerWave; ++s) {
-      const char* src = src_base[s] + (int64_t)kstep * kBK * 2;
+      const char* base = src_base[s] + (int64_t)kstep * kBK * 2;
       // Issued from asm, as in the attention kernel: the compiler's wait
       // model would otherwise hold every later LDS read until this DMA
       // lands.  Completion is awaited before each barrier.  The instruction
       // writes LDS only and has no destination registers.
       const uint32_t ldsa = __builtin_amdgcn_readfirstlane(
-          (uint32_t)(uintptr_t)&lds[stage][1024 * (8 * s + wave)]);
-      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+          (uint32_t)(uintptr_t)&lds[stage * kStage + 1024 * (8 * s + wave_u)]);
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                    :
-                   : "v"(src), "s"(ldsa)
+                   : "v"(src_off[s]), "s"(base), "s"(ldsa)
                    : "memory", "m0");
     }
   };
 
   // operand reads: A = W rows (features), B = X rows (tokens), each lane
-  // row l32 of a 32-row block at k = 8*hf + [0, 8) of the 16-wide k step
+  // row l32 of a 32-row block, granule 2c + hf (k = 16c + 8hf + [0, 8)) of
+  // k step c, found in slot (2c + hf) ^ swz(l32) (swz only sees l32)
   const int wn = (wave & 1) * 128;   // this wave's features within the tile
   const int wm = (wave >> 1) * 64;   // this wave's tokens within the tile
-  const int a_off = (wn + l32) * kRow + hf * 16;
-  const int b_off = kOpTile + (wm + l32) * kRow + hf * 16;
+  const int sw = swz(l32);
+  int a_off[4], b_off[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    a_off[c] = (wn + l32) * kRow + 16 * ((2 * c + hf) ^ sw);
+    b_off[c] = kOpTile + (wm + l32) * kRow + 16 * ((2 * c + hf) ^ sw);
+  }
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -136,19 +155,25 @@ __global__ void __launch_bounds__(kThreads, 1) linear_bf16_kernel(LinearParams p
   for (int s = 0; s < nk; ++s) {
     const int st = s & 1;
     if (s + 1 < nk) issue(s + 1, st ^ 1);  // its stage was last read in step s-1
-    const char* base = &lds[st][0];
+    const char* base = &lds[st * kStage];
     bf16x8 a[2][4], b[2][2];
     auto load = [&](int c, int buf) __attribute__((always_inline)) {
+      // in the order of first use: b0, a0, b1, a1, a2, a3
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        a[buf][nb] = __builtin_bit_cast(
-            bf16x8, *(const lds_u32x4*)(base + a_off + nb * 32 * kRow + c * 32));
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        b[buf][mb] = __builtin_bit_cast(
-            bf16x8, *(const lds_u32x4*)(base + b_off + mb * 32 * kRow + c * 32));
+      for (int i = 0; i < 6; ++i) {
+        if (i == 0 || i == 2) {
+          const int mb = i / 2;
+          b[buf][mb] = __builtin_bit_cast(
+              bf16x8, *(const lds_u32x4*)(base + b_off[c] + mb * 32 * kRow));
+        } else {
+          const int nb = i == 1 ? 0 : i - 2;
+          a[buf][nb] = __builtin_bit_cast(
+              bf16x8, *(const lds_u32x4*)(base + a_off[c] + nb * 32 * kRow));
+        }
+      }
     };
     load(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       if (c + 1 < 4) load(c + 1, (c + 1) & 1);
@@ -158,13 +183,24 @@ __global__ void __launch_bounds__(kThreads, 1) linear_bf16_kernel(LinearParams p
         for (int mb = 0; mb < 2; ++mb)
           acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c & 1][nb], b[c & 1][mb],
                                                                 acc[nb][mb], 0, 0, 0);
+      // one operand read of the next k step, then one MFMA, six times; then
+      // the last two MFMAs
+      if (c + 1 < 4) {
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // the next stage has landed
     __syncthreads();                     // and every wave is done with this one
   }
 
   // ---- epilogue: bias, bf16, staged in LDS as [token][feature] rows
-  char* out_tile = &lds[0][0];
+  char* out_tile = &lds[0];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll

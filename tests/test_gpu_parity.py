@@ -485,3 +485,33 @@ def test_rows_n100_one_of_eight(vga):
     ref = oracle.attention(oracle.MODE_SGA, qh, kh, vh, 100, L, 37, 37, 0.125, oracle_sga(sga),
                            rows=rows)
     check(host(out[torch.from_numpy(rows - r0).cuda()]), ref, "bf16", "N=100 rows sga")
+
+
+def test_block_n100_full_size(vga):
+    # a whole global block at 100 frames, as the block benchmark runs it: the
+    # QKV projection (137,400 x 1024 -> 3 x 1024, a ragged last token tile),
+    # exact global attention and the output projection, on sampled rows
+    N, gh, gw, S, H = 100, 37, 37, 5, 16
+    frames = vga.Frames(N, gh, gw, S, H)
+    T, L, C = frames.tokens, frames.tokens_per_frame, 64 * H
+    x, w, b, wo, bo = vga_inputs.feature_field_block(N, gh, gw, S, H, seed=12, device="cuda")
+    rows = _rows_with_tail(T, 48, 49, L)
+    sel = torch.from_numpy(rows).cuda()
+    say("case block-N100 qkv_proj T=%d" % T)
+    q, k, v = vga.qkv_proj(x, w, b, frames)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.qkv_proj(host(x[sel]), host(w), host(b), H)
+    for name, got, ref in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
+        check_linear(host(got[sel]), ref, "bf16", "block qkv %s" % name)
+    say("case block-N100 global")
+    o = vga.global_attn(q, k, v, frames)
+    torch.cuda.synchronize()
+    ref = oracle.attention(oracle.MODE_GLOBAL, host(q), host(k), host(v), N, L, gh, gw, 0.125,
+                           rows=rows)
+    check(host(o[sel]), ref, "bf16", "block global")
+    say("case block-N100 out_proj")
+    y = vga.out_proj(o, wo, bo, frames)
+    torch.cuda.synchronize()
+    assert y.shape == (T, C)
+    ry = oracle.linear(host(o[sel]).reshape(len(rows), C), host(wo), host(bo))
+    check_linear(host(y[sel]), ry, "bf16", "block out")
