@@ -9,10 +9,11 @@
 //     (r, c) of frame f has rank f*kpf + ((r-oh)/sh)*nw + (c-ow)/sw, special
 //     token u has rank f*kpf + nh*nw + (u - gh*gw) -- writes keep_mask[t]
 //     and keep_idx[rank] = t, and leaves the rank (or -1) in LDS;
-//  2. all threads stream the rows as 16-byte chunks (fully coalesced): kept
-//     rows are copied to Kc/Vc[rank], dropped rows are summed into per-thread
-//     fp32 partials, combined in a fixed order into partials[block] (no
-//     float atomics).
+//  2. all threads stream the rows as 16-byte chunks (fully coalesced; K and
+//     V are read once, so with non-temporal loads that do not displace
+//     cached lines): kept rows are copied to Kc/Vc[rank], dropped rows are
+//     summed into per-thread fp32 partials, combined in a fixed order into
+//     partials[block] (no float atomics).
 // sga_reduce_kernel sums the block partials in a fixed order and divides by
 // |D|, giving kmean and vmean [H, 64] in fp32.  Both are HBM-bound streaming
 // passes.
@@ -102,7 +103,8 @@ __global__ void __launch_bounds__(kGatherThreads) sga_gather_kernel(GatherParams
     for (; tok + G * (kUnroll - 1) < t_end; tok += G * kUnroll) {
       u32x4 w[kUnroll];
 #pragma unroll
-      for (int uu = 0; uu < kUnroll; ++uu) w[uu] = src[(size_t)(tok + G * uu) * W];
+      for (int uu = 0; uu < kUnroll; ++uu)
+        w[uu] = __builtin_nontemporal_load(&src[(size_t)(tok + G * uu) * W]);
 #pragma unroll
       for (int uu = 0; uu < kUnroll; ++uu) {
         const int32_t r = rank_of[tok + G * uu - t_begin];
@@ -113,7 +115,7 @@ __global__ void __launch_bounds__(kGatherThreads) sga_gather_kernel(GatherParams
       }
     }
     for (; tok < t_end; tok += G) {
-      const u32x4 w = src[(size_t)tok * W];
+      const u32x4 w = __builtin_nontemporal_load(&src[(size_t)tok * W]);
       const int32_t r = rank_of[tok - t_begin];
       if (r >= 0)
         dst[(size_t)r * W] = w;
