@@ -45,6 +45,7 @@ EXPORTS = ["vga_frame_attn", "vga_global_attn", "vga_sga_workspace_layout",
            "vga_sga_attn", "vga_register_workspace_layout", "vga_register_attn",
            "vga_layer_schedule", "vga_layer_schedule_register",
            "vga_frame_attn_rows", "vga_global_attn_rows", "vga_sga_attn_rows",
+           "vga_sga_select",
            "vga_qkv_proj", "vga_out_proj",
            "vga_status_string", "vga_last_error", "vga_abi_version"]
 
@@ -144,6 +145,9 @@ def _load():
     lib.vga_sga_attn.restype = ctypes.c_int
     lib.vga_sga_attn.argtypes = [ctypes.POINTER(CFrames), ctypes.POINTER(CSga), vp, vp, vp,
                                  vp, vp, ctypes.c_size_t, vp]
+    lib.vga_sga_select.restype = ctypes.c_int
+    lib.vga_sga_select.argtypes = [ctypes.POINTER(CFrames), ctypes.POINTER(CSga), vp, vp, vp,
+                                   ctypes.c_size_t, vp]
     lib.vga_layer_schedule.restype = ctypes.c_int
     lib.vga_layer_schedule.argtypes = [i32, i32, ctypes.POINTER(CSga), ctypes.POINTER(CLayer)]
     lib.vga_layer_schedule_register.restype = ctypes.c_int
@@ -274,8 +278,26 @@ def sga_attn(q, k, v, frames: Frames, sga: Sga, out=None, workspace=None):
     return out, workspace
 
 
+def sga_select(k, v, frames: Frames, sga: Sga, workspace=None):
+    """The SGA key selection, compaction and dropped mean alone (what
+    sga_attn does before its attention).  Returns the workspace, whose
+    sections ``workspace_views`` reads."""
+    import torch
+    _prepare(k, k, v, frames, k)
+    code = _dtype_code(k)
+    lay = sga_workspace_layout(frames, sga, code)
+    if workspace is None or workspace.numel() < lay.total:
+        workspace = torch.empty(int(lay.total), dtype=torch.uint8, device=k.device)
+    cf = frames.c(code)
+    cs = sga.c()
+    _check(lib.vga_sga_select(ctypes.byref(cf), ctypes.byref(cs), k.data_ptr(), v.data_ptr(),
+                              workspace.data_ptr(), workspace.numel(), _stream(k.device)))
+    return workspace
+
+
 def workspace_views(workspace, frames: Frames, sga: Sga, dtype_code: int = VGA_BF16):
-    """Views of the SGA workspace sections (after a vga_sga_attn call)."""
+    """Views of the SGA workspace sections (after a vga_sga_attn or
+    vga_sga_select call)."""
     import torch
     lay = sga_workspace_layout(frames, sga, dtype_code)
     H, D = frames.num_heads, frames.head_dim

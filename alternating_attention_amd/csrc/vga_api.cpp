@@ -229,6 +229,42 @@ vga_status dense_attn(vga::KeyRange kr, const vga_frames* s, int64_t r0, int64_t
   return finish(launch_flash(s, kr, p, hs), hs, what);
 }
 
+// The SGA workspace: present, 16-byte aligned and large enough.
+vga_status check_workspace(const vga_sga_ws_layout& w, const void* workspace,
+                           size_t workspace_bytes) {
+  if (!workspace) return fail(VGA_ERR_WORKSPACE, "workspace is NULL");
+  if ((uintptr_t)workspace % 16) return fail(VGA_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (workspace_bytes < w.total)
+    return fail(VGA_ERR_WORKSPACE, "workspace holds %zu bytes, needs %llu", workspace_bytes,
+                (unsigned long long)w.total);
+  return VGA_OK;
+}
+
+// Launch the SGA selection, gather and mean over all T tokens into the
+// workspace (its layout w); returns the gather parameters for the attention.
+hipError_t launch_select(const vga_frames* shape, const Checked& c, const vga::SgaGrid& g,
+                         const vga_sga_ws_layout& w, const void* k, const void* v,
+                         void* workspace, hipStream_t hs, vga::GatherParams* out) {
+  char* ws = (char*)workspace;
+  vga::GatherParams& gp = *out;
+  memset(&gp, 0, sizeof gp);
+  gp.k = k;
+  gp.v = v;
+  gp.kc = ws + w.kc;
+  gp.vc = ws + w.vc;
+  gp.keep_idx = (int32_t*)(ws + w.keep_idx);
+  gp.keep_mask = (uint8_t*)(ws + w.keep_mask);
+  gp.partials = (float*)(ws + w.partials);
+  gp.kmean = (float*)(ws + w.kmean);
+  gp.vmean = (float*)(ws + w.vmean);
+  gp.T = c.T;
+  gp.H = shape->num_heads;
+  gp.blocks = (int32_t)w.partial_blocks;
+  gp.num_dropped = w.num_dropped;
+  gp.grid = g;
+  return vga::launch_sga_gather(shape->dtype == VGA_BF16, gp, hs);
+}
+
 // SGA on query rows [r0, r1): selection, gather and mean over all T tokens,
 // then the shared-softmax attention for the rows.
 vga_status sga_run(const vga_frames* shape, const vga_sga* sga, int64_t r0, int64_t r1,
@@ -249,11 +285,8 @@ vga_status sga_run(const vga_frames* shape, const vga_sga* sga, int64_t r0, int6
   const vga::SgaGrid g = make_grid(shape, r);
   vga_sga_ws_layout w;
   fill_layout(shape, c, g, &w);
-  if (!workspace) return fail(VGA_ERR_WORKSPACE, "workspace is NULL");
-  if ((uintptr_t)workspace % 16) return fail(VGA_ERR_ALIGN, "workspace is not 16-byte aligned");
-  if (workspace_bytes < w.total)
-    return fail(VGA_ERR_WORKSPACE, "workspace holds %zu bytes, needs %llu", workspace_bytes,
-                (unsigned long long)w.total);
+  st = check_workspace(w, workspace, workspace_bytes);
+  if (st != VGA_OK) return st;
   const size_t rb = row_bytes(shape) * (size_t)(r1 - r0);
   if (overlaps(o, rb, workspace, w.total))
     return fail(VGA_ERR_ALIAS, "o overlaps the workspace");
@@ -264,22 +297,7 @@ vga_status sga_run(const vga_frames* shape, const vga_sga* sga, int64_t r0, int6
   char* ws = (char*)workspace;
   hipStream_t hs = (hipStream_t)stream;
   vga::GatherParams gp;
-  memset(&gp, 0, sizeof gp);
-  gp.k = k;
-  gp.v = v;
-  gp.kc = ws + w.kc;
-  gp.vc = ws + w.vc;
-  gp.keep_idx = (int32_t*)(ws + w.keep_idx);
-  gp.keep_mask = (uint8_t*)(ws + w.keep_mask);
-  gp.partials = (float*)(ws + w.partials);
-  gp.kmean = (float*)(ws + w.kmean);
-  gp.vmean = (float*)(ws + w.vmean);
-  gp.T = c.T;
-  gp.H = shape->num_heads;
-  gp.blocks = (int32_t)w.partial_blocks;
-  gp.num_dropped = w.num_dropped;
-  gp.grid = g;
-  hipError_t e = vga::launch_sga_gather(shape->dtype == VGA_BF16, gp, hs);
+  hipError_t e = launch_select(shape, c, g, w, k, v, workspace, hs, &gp);
   if (e != hipSuccess) return finish(e, hs, what);
 
   vga::FlashParams p = base_params(shape, c, q, ws + w.kc, ws + w.vc, o);
@@ -447,6 +465,30 @@ vga_status vga_sga_attn(const vga_frames* shape, const vga_sga* sga, const void*
                         size_t workspace_bytes, void* stream) {
   return sga_run(shape, sga, 0, 0, false, q, k, v, o, workspace, workspace_bytes, stream,
                  "vga_sga_attn");
+}
+
+vga_status vga_sga_select(const vga_frames* shape, const vga_sga* sga, const void* k,
+                          const void* v, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  Checked c;
+  vga_status st = check_shape(shape, &c);
+  if (st != VGA_OK) return st;
+  vga_sga r;
+  st = resolve_sga(shape, sga, &r);
+  if (st != VGA_OK) return st;
+  if (!k || !v) return fail(VGA_ERR_NULL, "k and v must be non-NULL");
+  if ((uintptr_t)k % 16 || (uintptr_t)v % 16)
+    return fail(VGA_ERR_ALIGN, "k and v must be 16-byte aligned");
+  const vga::SgaGrid g = make_grid(shape, r);
+  vga_sga_ws_layout w;
+  fill_layout(shape, c, g, &w);
+  st = check_workspace(w, workspace, workspace_bytes);
+  if (st != VGA_OK) return st;
+  if (overlaps(k, c.bytes, workspace, w.total) || overlaps(v, c.bytes, workspace, w.total))
+    return fail(VGA_ERR_ALIAS, "an input overlaps the workspace");
+  hipStream_t hs = (hipStream_t)stream;
+  vga::GatherParams gp;
+  return finish(launch_select(shape, c, g, w, k, v, workspace, hs, &gp), hs, "vga_sga_select");
 }
 
 vga_status vga_sga_attn_rows(const vga_frames* shape, const vga_sga* sga, int64_t row_begin,

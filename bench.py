@@ -439,10 +439,37 @@ def run(args):
                      "tflops": flop / (avg * 1e-3) / 1e12,
                      "frac_mfma_peak": flop / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                      "tokens_per_s": T / (avg * 1e-3)}
+    rows = {}
     if "sga" in per:
         gb = bytes_gather(T, nk, H)
         per["sga"]["gather_bytes"] = gb
         per["sga"]["kept_per_frame"] = int(lay.kept_per_frame)
+        # the selection, gather and mean alone (the HBM-bound part of the SGA
+        # call), timed after the steps on the same inputs and workspace
+        sel = Timer(torch)
+        for _ in range(10):
+            with sel:
+                vga.sga_select(k, v, frames, sga, ws)
+        torch.cuda.synchronize()
+        sms = float(np.median(sel.ms()))
+        per["sga_select"] = {"ms_per_call": sms, "calls_per_step": 0.0,
+                             "gb_per_s": gb / (sms * 1e-3) / 1e9,
+                             "frac_hbm_peak": gb / (sms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        att = per["sga"]["ms_per_call"] - sms
+        fl_sga = work["sga"] / per["sga"]["calls_per_step"]
+        rows["a3_a4_sga_select"] = {"bound": "hbm", "achieved": gb / (sms * 1e-3) / 1e9,
+                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                    "frac": gb / (sms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                    "algorithmic_bytes": gb, "ms": sms}
+        rows["a5_sga_attention"] = {"bound": "mfma", "achieved": fl_sga / (att * 1e-3) / 1e12,
+                                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                    "frac": fl_sga / (att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                    "ms": att, "note": "SGA call minus the selection call"}
+    for name, row in (("frame", "a1_frame"), ("global", "a2_global")):
+        if name in per:
+            rows[row] = {"bound": "mfma", "achieved": per[name]["tflops"],
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": per[name]["frac_mfma_peak"], "ms": per[name]["ms_per_call"]}
 
     extra = {}
     if args.workload == "n800reg":
@@ -559,7 +586,7 @@ def run(args):
                 "weights (no dataset, no trained weights)",
         "config": {"workload": desc, "frames": N, "tokens_per_frame": L, "tokens": T,
                    "heads": H, "head_dim": HEAD_DIM},
-        "roofline": roofline, "modes": per, "wall_s_timed": wall,
+        "roofline": roofline, "rows": rows, "modes": per, "wall_s_timed": wall,
         "gpu_state": {"before": state_before, "during": watch.summary(), "after": state_after},
     }
     result.update(extra)

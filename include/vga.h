@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define VGA_ABI_VERSION 3
+#define VGA_ABI_VERSION 4
 
 typedef enum {
   VGA_OK = 0,
@@ -171,6 +171,17 @@ vga_status vga_sga_workspace_layout(const vga_frames* shape, const vga_sga* sga,
 vga_status vga_sga_attn(const vga_frames* shape, const vga_sga* sga, const void* q,
                         const void* k, const void* v, void* o, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/* The key selection and compaction of SGA alone (AVGGT section 3, step two:
+ * uniform grid sampling and the mean of the dropped columns): fills the
+ * workspace sections keep_idx, keep_mask, kmean, vmean, kc and vc (and the
+ * partials) exactly as vga_sga_attn does before its attention, from K and
+ * V ([T, H, 64], 16-byte aligned); no output tensor.  Same workspace rules
+ * and errors as vga_sga_attn (VGA_ERR_NULL for k or v, VGA_ERR_ALIAS when k
+ * or v overlaps the workspace).  Reads K and V once: the HBM-bound step. */
+vga_status vga_sga_select(const vga_frames* shape, const vga_sga* sga, const void* k,
+                          const void* v, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* Per-layer schedule of the training-free pipeline (AVGGT section 3):
  * slot g < num_early_to_frame becomes VGA_MODE_FRAME; the remaining slots

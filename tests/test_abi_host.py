@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(vga):
 
 
 def test_abi_version_and_strings(vga):
-    assert vga.abi_version() == 3
+    assert vga.abi_version() == 4
     for code, name in enumerate(vga.STATUS_NAMES):
         assert vga.status_string(code) == name
 
@@ -111,6 +111,32 @@ def test_sga_validation(vga):
     assert call(vga.Sga(), ws=FAKE + 0x3000000 + 256) == 6  # o overlaps workspace
     assert vga.lib.vga_sga_attn(ctypes.byref(cf), None, FAKE, FAKE, FAKE, FAKE, FAKE, 1,
                                 None) == 1
+
+
+def test_select_validation(vga):
+    # every rejected call returns before any launch (fake device pointers)
+    f = _frames(vga)
+    cf = f.c(vga.VGA_BF16)
+
+    def call(sga, k=FAKE + 0x1000000, v=FAKE + 0x2000000, ws=FAKE + 0x4000000,
+             nbytes=1 << 30):
+        cs = sga.c()
+        return vga.lib.vga_sga_select(ctypes.byref(cf), ctypes.byref(cs), k, v, ws, nbytes, None)
+
+    assert call(vga.Sga(stride_h=0)) == 4
+    assert call(vga.Sga(mean_fill=3)) == 4
+    assert call(vga.Sga(), k=None) == 1
+    assert call(vga.Sga(), v=None) == 1
+    assert call(vga.Sga(), k=FAKE + 0x1000004) == 5
+    assert call(vga.Sga(), ws=None) == 7
+    assert call(vga.Sga(), nbytes=100) == 7
+    assert call(vga.Sga(), ws=FAKE + 0x4000008) == 5
+    assert call(vga.Sga(), ws=FAKE + 0x2000000 + 256) == 6  # v overlaps the workspace
+    assert vga.lib.vga_sga_select(ctypes.byref(cf), None, FAKE, FAKE, FAKE, 1, None) == 1
+    bad = f.c(vga.VGA_BF16)
+    bad.head_dim = 32
+    assert vga.lib.vga_sga_select(ctypes.byref(bad), ctypes.byref(vga.Sga().c()),
+                                  FAKE, FAKE, FAKE, 1 << 30, None) == 8
 
 
 def test_rows_validation(vga):

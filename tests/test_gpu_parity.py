@@ -515,3 +515,32 @@ def test_block_n100_full_size(vga):
     assert y.shape == (T, C)
     ry = oracle.linear(host(o[sel]).reshape(len(rows), C), host(wo), host(bo))
     check_linear(host(y[sel]), ry, "bf16", "block out")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_sga_select_matches_attn(vga, dt):
+    # the selection call alone leaves the same workspace (bit for bit) as the
+    # attention call: same kernels, fixed-order sums; checked against the
+    # oracle's selection and mean too
+    frames = vga.Frames(3, 7, 9, 3, 2)
+    T = frames.tokens
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    q, k, v = to_dev(tiny_qkv(T, 2, 64, seed=77), tdt)
+    code = vga.VGA_F32 if dt == "f32" else vga.VGA_BF16
+    for p in (vga.Sga(2, 2, 0, 0), vga.Sga(3, 2, 1, 1, False, 2)):
+        say("case select-%s %s" % (dt, p))
+        _, ws_a = vga.sga_attn(q, k, v, frames, p)
+        ws_b = vga.sga_select(k, v, frames, p)
+        torch.cuda.synchronize()
+        a, b = vga.workspace_views(ws_a, frames, p, code), vga.workspace_views(ws_b, frames, p, code)
+        for name in ("keep_idx", "keep_mask", "kmean", "vmean", "kc", "vc"):
+            assert torch.equal(a[name], b[name]), name
+        r = resolved(p, vga)
+        idx, mask = oracle.select(3, frames.tokens_per_frame, 7, 9, r.stride_h, r.stride_w,
+                                  r.phase_h, r.phase_w)
+        assert np.array_equal(b["keep_idx"].cpu().numpy().astype(np.int64), idx)
+        km, vm, nd = oracle.dropped_mean(host(k), host(v), 3, frames.tokens_per_frame, 7, 9,
+                                         r.stride_h, r.stride_w, r.phase_h, r.phase_w)
+        assert nd > 0
+        assert np.max(np.abs(b["kmean"].cpu().numpy() - km)) <= 1e-5
+        assert np.max(np.abs(b["vmean"].cpu().numpy() - vm)) <= 1e-5
