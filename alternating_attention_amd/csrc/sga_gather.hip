@@ -142,10 +142,11 @@ __global__ void __launch_bounds__(kGatherThreads) sga_gather_kernel(GatherParams
 }
 
 // Fixed-order reduction of the block partials: thread (quad q, group g)
-// sums 4 adjacent columns over blocks b = g, g + 16, ...; the 16 group sums
-// are then added pairwise in a fixed tree.
-constexpr int kReduceQuads = 64;
-constexpr int kReduceGroups = 16;
+// sums 4 adjacent columns over blocks b = g, g + 128, ...; the 128 group
+// sums are then added pairwise in a fixed tree.  Eight quads per workgroup
+// spread the partials over 2C/32 workgroups.
+constexpr int kReduceQuads = 8;
+constexpr int kReduceGroups = 128;
 
 __global__ void __launch_bounds__(kReduceQuads * kReduceGroups) sga_reduce_kernel(GatherParams p) {
   __shared__ f32x4 part[kReduceGroups][kReduceQuads];
