@@ -53,12 +53,15 @@ vga_status check_shape(const vga_frames* s, Checked* c) {
   if (s->tokens_per_frame < 1 || patches + s->num_special != s->tokens_per_frame)
     return fail(VGA_ERR_SHAPE, "tokens_per_frame %d != grid %dx%d + %d specials",
                 s->tokens_per_frame, s->grid_h, s->grid_w, s->num_special);
+  if (s->num_heads > 64 / (s->dtype == VGA_F32 ? 2 : 1))
+    return fail(VGA_ERR_UNSUPPORTED, "num_heads %d above the supported maximum", s->num_heads);
+  // T < 2^31 first, so that T*H*64 (H <= 64) cannot overflow
   const int64_t T = (int64_t)s->num_frames * s->tokens_per_frame;
+  if (T >= ((int64_t)1 << 31))
+    return fail(VGA_ERR_SHAPE, "T = %lld tokens exceeds 2^31", (long long)T);
   const int64_t elems = T * s->num_heads * vga::kHeadDim;
   if (elems >= ((int64_t)1 << 31))
     return fail(VGA_ERR_SHAPE, "T*H*64 = %lld exceeds 2^31 elements", (long long)elems);
-  if (s->num_heads > 64 / (s->dtype == VGA_F32 ? 2 : 1))
-    return fail(VGA_ERR_UNSUPPORTED, "num_heads %d above the supported maximum", s->num_heads);
   if (!(s->scale == s->scale) || isinf(s->scale))
     return fail(VGA_ERR_PARAM, "scale is not finite");
   c->T = T;

@@ -90,6 +90,19 @@ def test_validation_statuses(vga):
     assert vga.lib.vga_frame_attn(ctypes.byref(ok), None, FAKE, FAKE, FAKE, None) == 1
 
 
+def test_huge_shapes_rejected_before_overflow(vga):
+    # N = L = 2^30 with 64 heads: T*H*64 = 2^72 would wrap to 0 in 64 bits;
+    # the token count is checked on its own first, so the call is refused
+    f = vga.Frames(1 << 30, 1, 1 << 30, 0, 64)
+    cf = f.c(vga.VGA_BF16)
+    assert vga.lib.vga_global_attn(ctypes.byref(cf), FAKE, FAKE + 0x1000000, FAKE + 0x2000000,
+                                   FAKE + 0x3000000, None) == 2
+    assert "exceeds 2^31" in vga.last_error()
+    f = vga.Frames(1 << 16, 1, 1 << 15, 0, 1)     # T = 2^31 exactly
+    assert vga.lib.vga_frame_attn(ctypes.byref(f.c(vga.VGA_BF16)), FAKE, FAKE + 0x1000000,
+                                  FAKE + 0x2000000, FAKE + 0x3000000, None) == 2
+
+
 def test_sga_validation(vga):
     f = _frames(vga)
     cf = f.c(vga.VGA_BF16)
