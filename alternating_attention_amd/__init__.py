@@ -107,10 +107,14 @@ class Frames:
         return self.num_frames * self.tokens_per_frame
 
     def c(self, dtype_code: int, tokens_per_frame: int | None = None) -> CFrames:
-        return CFrames(self.num_frames,
-                       self.tokens_per_frame if tokens_per_frame is None else tokens_per_frame,
-                       self.grid_h, self.grid_w, self.num_special, self.num_heads,
-                       self.head_dim, dtype_code, self.scale)
+        ints = (self.num_frames,
+                self.tokens_per_frame if tokens_per_frame is None else tokens_per_frame,
+                self.grid_h, self.grid_w, self.num_special, self.num_heads, self.head_dim,
+                dtype_code)
+        # ctypes would wrap larger values silently
+        if any(not -(1 << 31) <= int(x) < (1 << 31) for x in ints):
+            raise ValueError("frame descriptor field outside int32: %r" % (ints,))
+        return CFrames(*ints, self.scale)
 
 
 @dataclass(frozen=True)

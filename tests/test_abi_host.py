@@ -98,6 +98,8 @@ def test_huge_shapes_rejected_before_overflow(vga):
     assert vga.lib.vga_global_attn(ctypes.byref(cf), FAKE, FAKE + 0x1000000, FAKE + 0x2000000,
                                    FAKE + 0x3000000, None) == 2
     assert "exceeds 2^31" in vga.last_error()
+    with pytest.raises(ValueError):
+        vga.Frames(1 << 31, 1, 1, 0, 1).c(vga.VGA_BF16)   # would wrap to -2^31
     f = vga.Frames(1 << 16, 1, 1 << 15, 0, 1)     # T = 2^31 exactly
     assert vga.lib.vga_frame_attn(ctypes.byref(f.c(vga.VGA_BF16)), FAKE, FAKE + 0x1000000,
                                   FAKE + 0x2000000, FAKE + 0x3000000, None) == 2
