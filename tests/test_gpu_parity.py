@@ -11,7 +11,9 @@ frames of 37x37+5 tokens, 16 heads, and the largest shape the ABI accepts,
 1,526 frames) compare seeded sampled rows, which the oracle computes one by
 one.  The same bars apply to register attention, the
 unit-weight mean column and the row-range calls (whose rows are also
-compared with the same rows of the full call).
+compared with the same rows of the full call).  Twenty seeded random small
+configurations (grid, specials, heads, SGA strides, phases and flags) add
+breadth in both element types.
 """
 import math
 import sys
@@ -544,3 +546,25 @@ def test_sga_select_matches_attn(vga, dt):
         assert nd > 0
         assert np.max(np.abs(b["kmean"].cpu().numpy() - km)) <= 1e-5
         assert np.max(np.abs(b["vmean"].cpu().numpy() - vm)) <= 1e-5
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_random_configurations(vga, seed):
+    # seeded random small configurations: frame count, grid, specials, heads,
+    # SGA strides, phases and flags, in both element types, every output
+    rng = np.random.default_rng(900 + seed)
+    N = int(rng.integers(1, 5))
+    gh, gw = int(rng.integers(1, 12)), int(rng.integers(1, 12))
+    S = int(rng.integers(0, 6))
+    H = int(rng.integers(1, 4))
+    dt = "f32" if seed % 2 == 0 else "bf16"
+    frames = vga.Frames(N, gh, gw, S, H)
+    q, k, v = to_dev(tiny_qkv(frames.tokens, H, 64, seed=1000 + seed),
+                     torch.float32 if dt == "f32" else torch.bfloat16)
+    sgas = []
+    for _ in range(3):
+        sh, sw = int(rng.integers(1, gh + 1)), int(rng.integers(1, gw + 1))
+        sgas.append(vga.Sga(sh, sw, int(rng.integers(-1, sh)), int(rng.integers(-1, sw)),
+                            bool(rng.integers(0, 2)), int(rng.integers(0, 3))))
+    run_and_compare(vga, frames, q, k, v, ["frame", "global", "register"], sgas,
+                    tag="random%d-%s N%d %dx%d S%d H%d" % (seed, dt, N, gh, gw, S, H))
