@@ -8,6 +8,8 @@ C names without the ``vga_`` prefix:
 * ``frame_attn(q, k, v, frames)``  -> vga_frame_attn
 * ``global_attn(q, k, v, frames)`` -> vga_global_attn
 * ``sga_attn(q, k, v, frames, sga)`` -> vga_sga_attn (+ workspace)
+* ``sga_select(k, v, frames, sga)`` -> vga_sga_select (the selection,
+  compaction and dropped mean alone; returns the workspace)
 * ``sga_workspace_layout(frames, sga)`` -> vga_sga_workspace_layout
 * ``register_attn(q, k, v, frames)`` -> vga_register_attn (+ workspace)
 * ``register_workspace_layout(frames)`` -> vga_register_workspace_layout
