@@ -456,6 +456,35 @@ def test_max_size_bf16(vga):
     check(host(out[torch.from_numpy(sel - r0).cuda()]), ref, "bf16", "max global rows")
 
 
+def test_projections_max_size_bf16(vga):
+    # the largest token count the ABI accepts at 16 heads (1,526 frames,
+    # T = 2,096,724): x is 4,294,090,752 bytes, so the kernel's 32-bit DMA
+    # offsets into x come within 876 KB of 2^32; sampled rows incl. the last
+    L, H = 37 * 37 + 5, 16
+    N = (2 ** 31 // (H * 64) - 1) // L
+    frames = vga.Frames(N, 37, 37, 5, H)
+    T, C = frames.tokens, 64 * H
+    assert T * C * 2 < 2 ** 32 < (T + 512) * C * 2
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    x = torch.randn(T, C, device="cuda", generator=g).to(torch.bfloat16)
+    w = (torch.randn(3 * C, C, device="cuda", generator=g) / 32).to(torch.bfloat16)
+    b = torch.randn(3 * C, device="cuda", generator=g).to(torch.bfloat16)
+    say("case proj-max T=%d" % T)
+    q, k, v = vga.qkv_proj(x, w, b, frames)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([seeded_rows(T, 24, 50), [0, T - 257, T - 256, T - 1]]))
+    sel = torch.from_numpy(rows).cuda()
+    rq, rk, rv = oracle.qkv_proj(host(x[sel]), host(w), host(b), H)
+    for name, got, ref in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
+        check_linear(host(got[sel]), ref, "bf16", "max qkv %s" % name)
+    del k, v
+    y = vga.out_proj(q, w[:C].contiguous(), None, frames)
+    torch.cuda.synchronize()
+    ry = oracle.linear(host(q[sel]).reshape(len(rows), C), host(w[:C].contiguous()))
+    check_linear(host(y[sel]), ry, "bf16", "max out")
+
+
 # ------------------------------------------------------------ row-range calls
 def _range_cases(T, L):
     # empty, one row, unaligned, tile-straddling, whole frames, everything
