@@ -136,7 +136,7 @@ def cpu_baseline(workload, frames, sga_list, modes, qkv_host, rows_count, seed=7
     dt = time.perf_counter() - t0
     step_s = dt * (r1 - r0) / rows_count
     return {"value": (r1 - r0) / step_s, "unit": "tokens/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "host": host_cpu(),
             "sample": "%d seeded query rows x %d heads of each layer of the step (%s), "
                       "timed %.1f s, extrapolated x %d/%d" % (
                           rows_count, frames.num_heads,
@@ -229,6 +229,19 @@ class SmiWatch:
                 "socket_power_w_median": pw[len(pw) // 2] if pw else None,
                 "socket_power_w_max": pw[-1] if pw else None,
                 "gfx_clk_mhz_median": clk[len(clk) // 2] if clk else None}
+
+
+def host_cpu():
+    """Model, logical CPUs and sockets of the host (from /proc/cpuinfo; best
+    effort: None where the file is missing)."""
+    try:
+        text = open("/proc/cpuinfo").read()
+    except OSError:
+        return None
+    models = [l.split(":", 1)[1].strip() for l in text.splitlines() if l.startswith("model name")]
+    sockets = {l.split(":", 1)[1].strip() for l in text.splitlines() if l.startswith("physical id")}
+    return {"model": models[0] if models else None, "logical_cpus": len(models),
+            "sockets": len(sockets) or None, "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
 def host_bits(t, torch):
