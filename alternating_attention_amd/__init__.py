@@ -18,6 +18,7 @@ C names without the ``vga_`` prefix:
 * ``qkv_proj(x, w, b, frames)`` -> vga_qkv_proj (returns q, k, v)
 * ``out_proj(o, w, b, frames)`` -> vga_out_proj
 * ``layer_schedule(num_global, num_early, sga)`` -> vga_layer_schedule
+* ``layer_schedule_sga(num_global, num_early, per_slot)`` -> vga_layer_schedule_sga
 * ``layer_schedule_register(num_global, num_early, register_every, sga)``
   -> vga_layer_schedule_register
 
@@ -45,7 +46,7 @@ MODE_FRAME, MODE_GLOBAL, MODE_SGA, MODE_REGISTER = 0, 1, 2, 3
 # every symbol include/vga.h declares
 EXPORTS = ["vga_frame_attn", "vga_global_attn", "vga_sga_workspace_layout",
            "vga_sga_attn", "vga_register_workspace_layout", "vga_register_attn",
-           "vga_layer_schedule", "vga_layer_schedule_register",
+           "vga_layer_schedule", "vga_layer_schedule_register", "vga_layer_schedule_sga",
            "vga_frame_attn_rows", "vga_global_attn_rows", "vga_sga_attn_rows",
            "vga_sga_select",
            "vga_qkv_proj", "vga_out_proj",
@@ -156,6 +157,8 @@ def _load():
                                    ctypes.c_size_t, vp]
     lib.vga_layer_schedule.restype = ctypes.c_int
     lib.vga_layer_schedule.argtypes = [i32, i32, ctypes.POINTER(CSga), ctypes.POINTER(CLayer)]
+    lib.vga_layer_schedule_sga.restype = ctypes.c_int
+    lib.vga_layer_schedule_sga.argtypes = [i32, i32, ctypes.POINTER(CSga), ctypes.POINTER(CLayer)]
     lib.vga_layer_schedule_register.restype = ctypes.c_int
     lib.vga_layer_schedule_register.argtypes = [i32, i32, i32, ctypes.POINTER(CSga),
                                                 ctypes.POINTER(CLayer)]
@@ -420,6 +423,19 @@ def layer_schedule(num_global: int, num_early: int, sga: Sga | None):
     cs = sga.c() if sga is not None else None
     _check(lib.vga_layer_schedule(num_global, num_early,
                                   ctypes.byref(cs) if cs is not None else None, arr))
+    return [(arr[i].mode, arr[i].sga) for i in range(num_global)]
+
+
+def layer_schedule_sga(num_global: int, num_early: int, per_slot):
+    """Per-slot SGA schedule: FRAME for the first num_early slots, then SGA
+    with per_slot[i] (a list of num_global - num_early Sga) for slot
+    num_early + i."""
+    n = num_global - num_early
+    arr = (CLayer * max(num_global, 1))()
+    sg = (CSga * max(len(per_slot), 1))(*[p.c() for p in per_slot])
+    if len(per_slot) != max(n, 0):
+        raise ValueError("need %d per-slot SGA parameters, got %d" % (max(n, 0), len(per_slot)))
+    _check(lib.vga_layer_schedule_sga(num_global, num_early, sg, arr))
     return [(arr[i].mode, arr[i].sga) for i in range(num_global)]
 
 

@@ -583,6 +583,35 @@ vga_status vga_layer_schedule_register(int32_t num_global_layers,
   return schedule(num_global_layers, num_early_to_frame, register_every, sga, out);
 }
 
+vga_status vga_layer_schedule_sga(int32_t num_global_layers, int32_t num_early_to_frame,
+                                  const vga_sga* per_slot_sga, vga_layer* out) {
+  if (num_global_layers < 0 || num_early_to_frame < 0 ||
+      num_early_to_frame > num_global_layers)
+    return fail(VGA_ERR_PARAM, "need 0 <= num_early (%d) <= num_global (%d)",
+                num_early_to_frame, num_global_layers);
+  const int32_t n_sga = num_global_layers - num_early_to_frame;
+  if (n_sga > 0 && !per_slot_sga) return fail(VGA_ERR_NULL, "per-slot SGA parameters are NULL");
+  if (num_global_layers > 0 && !out) return fail(VGA_ERR_NULL, "schedule output is NULL");
+  // every slot's parameters are checked before anything is written
+  for (int32_t i = 0; i < n_sga; ++i) {
+    vga_sga r;
+    const vga_status st = resolve_sga(nullptr, &per_slot_sga[i], &r);
+    if (st != VGA_OK) return st;
+  }
+  for (int32_t g = 0; g < num_global_layers; ++g) {
+    vga_layer l;
+    memset(&l, 0, sizeof l);
+    if (g < num_early_to_frame) {
+      l.mode = VGA_MODE_FRAME;
+    } else {
+      l.mode = VGA_MODE_SGA;
+      resolve_sga(nullptr, &per_slot_sga[g - num_early_to_frame], &l.sga);
+    }
+    out[g] = l;
+  }
+  return VGA_OK;
+}
+
 const char* vga_status_string(vga_status s) {
   switch (s) {
     case VGA_OK: return "VGA_OK";

@@ -103,13 +103,14 @@ class Timer:
 
 
 def cpu_baseline(workload, frames, sga_list, modes, qkv_host, rows_count, seed=7,
-                 row_range=None, proj=None):
+                 row_range=None, proj=None, counts=None):
     """The fp64 oracle on a bounded sample: `rows_count` seeded query rows
-    (all heads) of each mode of the step, extrapolated x (rows of the step) /
-    rows_count.  row_range: the step's query rows (default all T).  proj:
-    (x, w_qkv, b_qkv, w_o, b_o) host bits when every attention layer of the
-    step sits between a QKV and an output projection (their rows are timed
-    too)."""
+    (all heads) of each kind of layer of the step, each timed once, weighted
+    by how often the step runs it (`counts`, aligned with modes + sga_list;
+    default once each) and extrapolated x (rows of the step) / rows_count.
+    row_range: the step's query rows (default all T).  proj: (x, w_qkv, b_qkv,
+    w_o, b_o) host bits when every attention layer of the step sits between a
+    QKV and an output projection (their rows are timed too)."""
     import oracle
     q, k, v = qkv_host
     T = frames.tokens
@@ -117,30 +118,40 @@ def cpu_baseline(workload, frames, sga_list, modes, qkv_host, rows_count, seed=7
     rows = r0 + np.sort(np.random.default_rng(seed).choice(r1 - r0, size=rows_count,
                                                             replace=False))
     args = (frames.num_frames, frames.tokens_per_frame, frames.grid_h, frames.grid_w, 0.125)
-    t0 = time.perf_counter()
+    counts = counts or [1] * (len(modes) + len(sga_list))
+    assert len(counts) == len(modes) + len(sga_list)
+    layer_s = []
     for mode in modes:
         code = {"frame": oracle.MODE_FRAME, "global": oracle.MODE_GLOBAL,
                 "register": oracle.MODE_REGISTER}[mode]
+        t0 = time.perf_counter()
         oracle.attention(code, q, k, v, *args, rows=rows)
+        layer_s.append(time.perf_counter() - t0)
     for p in sga_list:
+        t0 = time.perf_counter()
         oracle.attention(oracle.MODE_SGA, q, k, v, *args,
                          dict(stride_h=p.stride_h, stride_w=p.stride_w, phase_h=p.phase_h,
                               phase_w=p.phase_w, diagonal=int(p.diagonal),
                               mean_fill=int(p.mean_fill)), rows=rows)
+        layer_s.append(time.perf_counter() - t0)
     if proj is not None:
         x, wqkv, bqkv, wo, bo = proj
         xr = np.ascontiguousarray(x[rows])
-        for _ in list(modes) + list(sga_list):
+        for i in range(len(layer_s)):
+            t0 = time.perf_counter()
             oracle.qkv_proj(xr, wqkv, bqkv, frames.num_heads)
             oracle.linear(xr, wo, bo)
-    dt = time.perf_counter() - t0
-    step_s = dt * (r1 - r0) / rows_count
+            layer_s[i] += time.perf_counter() - t0
+    dt = sum(layer_s)
+    step_s = sum(c * t for c, t in zip(counts, layer_s)) * (r1 - r0) / rows_count
     return {"value": (r1 - r0) / step_s, "unit": "tokens/s", "cores": oracle.max_threads(),
             "kind": "oracle", "host": host_cpu(),
-            "sample": "%d seeded query rows x %d heads of each layer of the step (%s), "
-                      "timed %.1f s, extrapolated x %d/%d" % (
+            "sample": "%d seeded query rows x %d heads of each kind of layer of the step "
+                      "(%s), timed %.1f s, weighted by its count in the step and "
+                      "extrapolated x %d/%d" % (
                           rows_count, frames.num_heads,
-                          "+".join(list(modes) + ["sga"] * len(sga_list))
+                          "+".join("%dx%s" % (c, n) for c, n in
+                                   zip(counts, list(modes) + ["sga"] * len(sga_list)))
                           + (", each with its QKV and output projections" if proj else ""),
                           dt, r1 - r0,
                           rows_count),
@@ -267,7 +278,8 @@ def run(args):
     import alternating_attention_amd as vga
     import vga_inputs
 
-    base = {"n800reg": "n800", "shard8": "n800", "sweep": "n300", "block": "n100"}
+    base = {"n800reg": "n800", "n800ramp": "n800", "shard8": "n800", "sweep": "n300",
+            "block": "n100"}
     w = vga_inputs.WORKLOADS[base.get(args.workload, args.workload)]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -280,6 +292,7 @@ def run(args):
     out = torch.empty_like(q)
     out_b = torch.empty_like(q)
     timers = {}
+    step_counts = None   # per kind of layer (modes, then SGA list) when the step repeats them
 
     def timed(name, fn):
         t = timers.setdefault(name, Timer(torch))
@@ -355,7 +368,37 @@ def run(args):
                     timed("sga", lambda: vga.sga_attn(q, k, v, frames, sga, out_b, ws))
         work = {"frame": 8 * flops_frame(N, L, H), "sga": 16 * flops_sga(T, nk, H)}
         dominant, modes, sgas = "sga", ["frame"], [sga]
+        step_counts = [8, 16]
         assert len(plan) == 24
+    elif args.workload == "n800ramp":
+        # per-layer strides: the SGA slots sample finely first, coarsely after
+        ramp = [vga.Sga(2, 2, 0, 0, True, True)] * 8 + [vga.Sga(3, 3, 1, 1, True, True)] * 8
+        plan = vga.layer_schedule_sga(24, 8, ramp)
+        lays = {(p.stride_h, p.stride_w): vga.sga_workspace_layout(frames, p) for p in ramp}
+        ws = torch.empty(int(max(l.total for l in lays.values())), dtype=torch.uint8, device=dev)
+        desc = ("N=800 frames x 1374 tokens = 1,099,200 tokens, 16 heads x 64, bf16; "
+                "step = a 24-slot schedule with per-layer strides: 8 frame layers, 8 SGA 2x2 "
+                "layers (phase 0), 8 SGA 3x3 layers (phase 1), all with diagonal and "
+                "mean-fill; exact global layer timed once beside it")
+
+        def as_sga(cs):
+            return vga.Sga(cs.stride_h, cs.stride_w, cs.phase_h, cs.phase_w, bool(cs.diagonal),
+                           cs.mean_fill)
+
+        def step():
+            for mode, cs in vga.layer_schedule_sga(24, 8, ramp):
+                if mode == vga.MODE_FRAME:
+                    timed("frame", lambda: vga.frame_attn(q, k, v, frames, out))
+                else:
+                    p = as_sga(cs)
+                    timed("sga_%dx%d" % (p.stride_h, p.stride_w),
+                          lambda p=p: vga.sga_attn(q, k, v, frames, p, out_b, ws))
+        work = {"frame": 8 * flops_frame(N, L, H),
+                "sga_2x2": 8 * flops_sga(T, int(lays[(2, 2)].num_kept), H),
+                "sga_3x3": 8 * flops_sga(T, int(lays[(3, 3)].num_kept), H)}
+        dominant, modes, sgas = "sga_2x2", ["frame"], [ramp[0], ramp[8]]
+        step_counts = [8, 8, 8]
+        assert [m for m, _ in plan] == [vga.MODE_FRAME] * 8 + [vga.MODE_SGA] * 16
     elif args.workload == "n800reg":
         sga = vga.Sga(3, 3, 1, 1, True, True)
         lay = vga.sga_workspace_layout(frames, sga)
@@ -546,6 +589,23 @@ def run(args):
             per[n]["kept_per_frame"] = int(lays[n].kept_per_frame)
             per[n]["speedup_vs_exact"] = gms / per[n]["ms_per_call"]
             per[n]["deviation_vs_exact"] = deviation(outs[n], out)
+    if args.workload == "n800ramp":
+        log("exact global layer, timed once")
+        g = Timer(torch)
+        with g:
+            vga.global_attn(q, k, v, frames, out)
+        torch.cuda.synchronize()
+        gms = g.ms()[0]
+        per["global_once"] = {"ms_per_call": gms,
+                              "tflops": flops_global(T, H) / (gms * 1e-3) / 1e12}
+        extra["schedule_vs_24_exact_speedup"] = 24 * gms / ms_step
+        for p in (ramp[0], ramp[8]):
+            name = "sga_%dx%d" % (p.stride_h, p.stride_w)
+            vga.sga_attn(q, k, v, frames, p, out_b, ws)
+            torch.cuda.synchronize()
+            per[name]["speedup_vs_exact"] = gms / per[name]["ms_per_call"]
+            per[name]["deviation_vs_exact"] = deviation(out_b, out)
+            per[name]["kept_per_frame"] = int(lays[(p.stride_h, p.stride_w)].kept_per_frame)
     if args.workload in ("n300", "n800"):
         if args.workload == "n800":
             log("exact global layer, timed once")
@@ -614,7 +674,7 @@ def run(args):
         result["cpu_baseline"] = cpu_baseline(
             w, frames, sgas, modes, qkv, args.cpu_rows,
             row_range=(3 * T // 8, 4 * T // 8) if args.workload == "shard8" else None,
-            proj=proj)
+            proj=proj, counts=step_counts)
     return result
 
 
@@ -637,7 +697,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="n100",
-                    choices=["n100", "n300", "n800", "n800reg", "shard8", "sweep", "block"])
+                    choices=["n100", "n300", "n800", "n800reg", "n800ramp", "shard8", "sweep",
+                             "block"])
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gpu-state", action="store_true",
@@ -652,7 +713,8 @@ def main():
         copy_probe()
         return
     defaults = {"n100": (30, 20), "n300": (3, 1), "n800": (1, 1), "n800reg": (2, 1),
-                "shard8": (2, 1), "sweep": (2, 1), "block": (10, 5)}[args.workload]
+                "n800ramp": (1, 0), "shard8": (2, 1), "sweep": (2, 1),
+                "block": (10, 5)}[args.workload]
     args.steps = args.steps if args.steps is not None else defaults[0]
     args.warmup = args.warmup if args.warmup is not None else defaults[1]
     res = run(args)

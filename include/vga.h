@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define VGA_ABI_VERSION 4
+#define VGA_ABI_VERSION 5
 
 typedef enum {
   VGA_OK = 0,
@@ -219,6 +219,19 @@ vga_status vga_layer_schedule_register(int32_t num_global_layers,
                                        int32_t num_early_to_frame,
                                        int32_t register_every, const vga_sga* sga,
                                        vga_layer* out);
+
+/* Schedule with per-slot SGA parameters (AVGGT section 3 names the stride
+ * as the knob and leaves its per-layer choice open): slot
+ * g < num_early_to_frame becomes VGA_MODE_FRAME; slot g >= num_early_to_frame
+ * becomes VGA_MODE_SGA with per_slot_sga[g - num_early_to_frame] (phases
+ * resolved), so that, e.g., later layers can sample more coarsely.
+ * per_slot_sga: host array of num_global_layers - num_early_to_frame
+ * entries (may be NULL when that is 0); out: host array of
+ * num_global_layers entries.  Host only.  Errors: VGA_ERR_PARAM (counts out
+ * of range, or any slot's strides/phases/flags), VGA_ERR_NULL; on error
+ * nothing is written to out. */
+vga_status vga_layer_schedule_sga(int32_t num_global_layers, int32_t num_early_to_frame,
+                                  const vga_sga* per_slot_sga, vga_layer* out);
 
 /* Row-range variants: the share of one device when the query rows are
  * split across devices (each device holds all of K and V and its own rows

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(vga):
 
 
 def test_abi_version_and_strings(vga):
-    assert vga.abi_version() == 4
+    assert vga.abi_version() == 5
     for code, name in enumerate(vga.STATUS_NAMES):
         assert vga.status_string(code) == name
 
@@ -283,6 +283,29 @@ def test_layer_schedule(vga):
         vga.layer_schedule(4, 1, vga.Sga(stride_h=0))
     assert vga.lib.vga_layer_schedule(3, 1, None, None) == 1
     assert vga.layer_schedule(0, 0, None) == []
+
+
+def test_layer_schedule_per_slot_sga(vga):
+    import oracle
+    ramp = [vga.Sga(2, 2, 0, 0)] * 8 + [vga.Sga(3, 3, -1, -1, False, 2)] * 8
+    sch = vga.layer_schedule_sga(24, 8, ramp)
+    assert [m for m, _ in sch] == list(oracle.schedule(24, 8, True))
+    assert all((s.stride_h, s.phase_h, s.diagonal, s.mean_fill) == (2, 0, 1, 1) for _, s in sch[8:16])
+    assert all((s.stride_w, s.phase_w, s.diagonal, s.mean_fill) == (3, 1, 0, 2) for _, s in sch[16:])
+    assert [m for m, _ in vga.layer_schedule_sga(3, 3, [])] == [vga.MODE_FRAME] * 3
+    with pytest.raises(ValueError):
+        vga.layer_schedule_sga(4, 1, [vga.Sga()] * 2)       # needs 3 entries
+    # a bad slot anywhere is refused before anything is written
+    out = (vga.CLayer * 4)()
+    for l in out:
+        l.mode = 77
+    bad = (vga.CSga * 3)(vga.Sga().c(), vga.Sga(stride_h=0).c(), vga.Sga().c())
+    assert vga.lib.vga_layer_schedule_sga(4, 1, bad, out) == 4
+    assert [l.mode for l in out] == [77] * 4
+    assert vga.lib.vga_layer_schedule_sga(4, 5, bad, out) == 4
+    assert vga.lib.vga_layer_schedule_sga(4, 1, None, out) == 1
+    assert vga.lib.vga_layer_schedule_sga(4, 1, bad, None) == 1
+    assert vga.lib.vga_layer_schedule_sga(2, 2, None, out) == 0
 
 
 def test_schedule_matches_oracle(vga):
