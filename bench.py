@@ -699,7 +699,9 @@ def main():
     ap.add_argument("--workload", default="n100",
                     choices=["n100", "n300", "n800", "n800reg", "n800ramp", "shard8", "sweep",
                              "block"])
-    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-rows", type=int, default=None,
+                    help="oracle rows per kind of layer (default 256; 128 for n800ramp, "
+                         "whose 2x2 rows span 292,800 keys)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gpu-state", action="store_true",
                     help="skip the amd-smi power and clock samples (for runs under a profiler)")
@@ -715,6 +717,8 @@ def main():
     defaults = {"n100": (30, 20), "n300": (3, 1), "n800": (1, 1), "n800reg": (2, 1),
                 "n800ramp": (1, 0), "shard8": (2, 1), "sweep": (2, 1),
                 "block": (10, 5)}[args.workload]
+    if args.cpu_rows is None:
+        args.cpu_rows = 128 if args.workload == "n800ramp" else 256
     args.steps = args.steps if args.steps is not None else defaults[0]
     args.warmup = args.warmup if args.warmup is not None else defaults[1]
     res = run(args)
