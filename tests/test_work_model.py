@@ -43,3 +43,29 @@ def test_sga_window_reduces_keys_by_stride_area():
     gh = gw = 8
     assert kept_per_frame_closed_form(gh, gw, 0, g["stride"], g["stride"], 0, 0) * g["stride"] ** 2 \
         == gh * gw * g["kept_per_full_window"]
+
+
+def test_cpu_baseline_weights_layers_by_count(monkeypatch):
+    # the step time is each kind of layer's oracle time on the sampled rows,
+    # weighted by how often the step runs it, scaled by rows of step / rows
+    import oracle
+    from vga_inputs import tiny_qkv
+
+    clock = iter([0.0, 1.0, 10.0, 12.0])       # frame layer 1 s, SGA layer 2 s
+    monkeypatch.setattr(bench.time, "perf_counter", lambda: next(clock))
+    monkeypatch.setattr(oracle, "attention", lambda *a, **k: None)
+
+    class F:  # the fields cpu_baseline reads
+        num_frames, tokens_per_frame, grid_h, grid_w, num_heads = 2, 69, 8, 8, 2
+        tokens = 138
+
+    class P:
+        stride_h = stride_w = 2
+        phase_h = phase_w = 0
+        diagonal, mean_fill = True, 1
+
+    q, k, v = tiny_qkv(138, 2, 64, seed=0)
+    res = bench.cpu_baseline("tiny", F, [P], ["frame"], (q, k, v), 23, counts=[2, 3])
+    assert abs(res["seconds_per_step"] - (2 * 1.0 + 3 * 2.0) * 138 / 23) < 1e-9
+    assert abs(res["value"] - 138 / res["seconds_per_step"]) < 1e-9
+    assert "2xframe+3xsga" in res["sample"]
