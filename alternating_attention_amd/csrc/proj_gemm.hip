@@ -74,12 +74,17 @@ __global__ void __launch_bounds__(kThreads, 1) linear_bf16_kernel(LinearParams p
   const int l32 = lane & 31, hf = lane >> 5;
   const uint32_t n_tiles = (uint32_t)((p.N + kBN - 1) / kBN);
   // Workgroup b runs on XCD b mod 8; each XCD takes one contiguous range of
-  // tiles, so the feature tiles of a token tile share its X rows in that
-  // XCD's L2.
+  // tiles (bl), in grouped order: 8 token tiles x every feature tile, token
+  // tile fastest, so that the ~32 tiles an XCD runs at once cover 8 token
+  // tiles x 4 feature tiles and share their X and W rows in its L2.
   const uint32_t nb = gridDim.x, x8 = blockIdx.x % 8u, per = nb / 8u, rem = nb % 8u;
   const uint32_t bl = x8 * per + min(x8, rem) + blockIdx.x / 8u;
-  const int64_t m0 = (int64_t)(bl / n_tiles) * kBM;
-  const int64_t n0 = (int64_t)(bl % n_tiles) * kBN;
+  const uint32_t m_tiles = (uint32_t)((p.M + kBM - 1) / kBM);
+  const uint32_t grp = bl / (8u * n_tiles), first_m = grp * 8u;
+  const uint32_t gsz = min(m_tiles - first_m, 8u);
+  const uint32_t in_grp = bl - grp * 8u * n_tiles;
+  const int64_t m0 = (int64_t)(first_m + in_grp % gsz) * kBM;
+  const int64_t n0 = (int64_t)(in_grp / gsz) * kBN;
   const int64_t K = p.K;
   const int nk = (int)(K / kBK);
 
