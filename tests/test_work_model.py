@@ -69,3 +69,10 @@ def test_cpu_baseline_weights_layers_by_count(monkeypatch):
     assert abs(res["seconds_per_step"] - (2 * 1.0 + 3 * 2.0) * 138 / 23) < 1e-9
     assert abs(res["value"] - 138 / res["seconds_per_step"]) < 1e-9
     assert "2xframe+3xsga" in res["sample"]
+
+
+def test_projection_flops():
+    # y = x W^T + b: one multiply-add per (token, input, output) feature
+    assert bench.flops_linear(137400, 1024, 3072) == 2 * 137400 * 1024 * 3072
+    # the QKV projection is three output projections' worth of work
+    assert bench.flops_linear(7, 64, 192) == 3 * bench.flops_linear(7, 64, 64)
