@@ -431,6 +431,11 @@ def test_n800_full_size_frame_sga(vga):
     rows = _rows_with_tail(frames.tokens, 32, 44, frames.tokens_per_frame)
     run_and_compare(vga, frames, q, k, v, ["frame", "register"], [vga.Sga(3, 3, 1, 1)],
                     rows=rows, tag="N=800")
+    # exact global attention over all 1,099,200 keys, on fewer sampled rows
+    # (the oracle's cost per row is the whole key set)
+    grow = np.unique(np.concatenate([seeded_rows(frames.tokens, 12, 46),
+                                     [0, frames.tokens - 1]]))
+    run_and_compare(vga, frames, q, k, v, ["global"], [], rows=grow, tag="N=800")
 
 
 def test_max_size_bf16(vga):
