@@ -218,18 +218,25 @@ def _dtype_code(t) -> int:
     raise TypeError("q/k/v must be float32 or bfloat16, got %s" % t.dtype)
 
 
-def _prepare(q, k, v, frames: Frames, out):
-    import torch
-    for name, t in (("q", q), ("k", k), ("v", v)):
+def _check_tokens(frames: Frames, **tensors):
+    """Every tensor a contiguous GPU [N*L, H, D] array, one dtype and device."""
+    first = next(iter(tensors.values()))
+    for name, t in tensors.items():
         if not t.is_cuda:
             raise ValueError("%s must be a GPU tensor" % name)
         if not t.is_contiguous():
             raise ValueError("%s must be contiguous" % name)
-        if t.dtype != q.dtype or t.shape != q.shape or t.device != q.device:
-            raise ValueError("q, k, v must share dtype, shape and device")
+        if t.dtype != first.dtype or t.shape != first.shape or t.device != first.device:
+            raise ValueError("%s must share dtype, shape and device" % ", ".join(tensors))
     expect = (frames.tokens, frames.num_heads, frames.head_dim)
-    if tuple(q.shape) != expect:
-        raise ValueError("q/k/v shape %s != [N*L, H, D] = %s" % (tuple(q.shape), expect))
+    if tuple(first.shape) != expect:
+        raise ValueError("%s shape %s != [N*L, H, D] = %s"
+                         % ("/".join(tensors), tuple(first.shape), expect))
+
+
+def _prepare(q, k, v, frames: Frames, out):
+    import torch
+    _check_tokens(frames, q=q, k=k, v=v)
     if out is None:
         out = torch.empty_like(q)
     elif (out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous()
@@ -292,7 +299,7 @@ def sga_select(k, v, frames: Frames, sga: Sga, workspace=None):
     sga_attn does before its attention).  Returns the workspace, whose
     sections ``workspace_views`` reads."""
     import torch
-    _prepare(k, k, v, frames, k)
+    _check_tokens(frames, k=k, v=v)
     code = _dtype_code(k)
     lay = sga_workspace_layout(frames, sga, code)
     if workspace is None or workspace.numel() < lay.total:

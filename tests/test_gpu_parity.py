@@ -295,6 +295,10 @@ def test_python_errors(vga):
     with pytest.raises(vga.VgaError) as ei:
         vga.global_attn(q, q, q, frames, out=q)       # o aliases q
     assert ei.value.status == 6
+    with pytest.raises(ValueError):
+        vga.sga_select(q, q.float(), frames, vga.Sga())
+    with pytest.raises(ValueError):
+        vga.sga_select(q[:8], q[:8], frames, vga.Sga())
 
 
 # --------------------------------------------- projections around a layer
