@@ -26,7 +26,8 @@
 // K/V tiles of 128 keys move global -> LDS with global_load_lds_dwordx4 (no
 // registers) through a ring of three stages (114 KB: one workgroup per CU);
 // a ragged last tile is taken first (softmax sums do not depend on the key
-// order), so every later tile is full and needs no masking.
+// order), so every later tile is full and needs no masking; the ragged tile
+// runs the same pipelined steps with its keys past the end masked.
 //
 // Software pipeline over 32-key sub-tiles j: step j issues the QK^T MFMAs
 // of sub-tile j+1 and the PV MFMAs of sub-tile j-1 while the VALU computes
@@ -371,10 +372,12 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
   // (K at stK/sbK) and PV of the previous one (V at stV/sbV, operand Pp)
   // on the matrix core, each MFMA followed by one pair of this sub-tile's
   // softmax (scores Sc -> Pc); the sched barriers pin that order.  Returns
-  // the lane sums of the rounded P in lt.
+  // the lane sums of the rounded P in lt.  Tail: the sub-tile's keys start
+  // at key0 and those at or past the end of the range get P = 0.
   auto step_fast = [&](int stK, int sbK, int stV, int sbV, const f32x16 (&Sc)[2],
                        u32x4 (&Pc)[2][2], f32x16 (&Sn)[2], const u32x4 (&Pp)[2][2],
-                       float (&lt)[2]) __attribute__((always_inline)) {
+                       float (&lt)[2], int64_t key0, auto tail_tag) __attribute__((always_inline)) {
+    constexpr bool tail = decltype(tail_tag)::value;
     const char* sk = &lds[stK][0] + kread + sbK * 32 * kKRow;
     const char* sv = &lds[stV][0] + vread + sbV * 32 * kVRow;
     // PV units first (they free Pp), then the QK units (they fill Sn); the
@@ -395,8 +398,13 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
     auto pair = [&](int u) __attribute__((always_inline)) {
       const int qb = u >> 3, c2 = (u >> 2) & 1, e = u & 3;
       const float nm = qb ? nm1 : nm0;
-      const float z0 = __builtin_fmaf(Sc[qb][8 * c2 + 2 * e], qscale, nm);
-      const float z1 = __builtin_fmaf(Sc[qb][8 * c2 + 2 * e + 1], qscale, nm);
+      float z0 = __builtin_fmaf(Sc[qb][8 * c2 + 2 * e], qscale, nm);
+      float z1 = __builtin_fmaf(Sc[qb][8 * c2 + 2 * e + 1], qscale, nm);
+      if constexpr (tail) {
+        const int64_t k0 = key0 + 16 * c2 + 8 * hf + 2 * e;
+        if (k0 >= tr.k_end) z0 = -INFINITY;
+        if (k0 + 1 >= tr.k_end) z1 = -INFINITY;
+      }
       const uint32_t pp = pack_bf16(__builtin_amdgcn_exp2f(z0), __builtin_amdgcn_exp2f(z1));
       Pc[qb][c2][e] = pp;
       lt[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), kOnes, lt[qb],
@@ -432,13 +440,21 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
   };
   // the rare exact redo after a fast step: raise m to the sub-tile max
   // (O and l rescaled) and recompute P
-  auto redo_exact = [&](const f32x16 (&S)[2], u32x4 (&P)[2][2], float (&lt)[2])
-      __attribute__((always_inline)) {
+  // (tail: only the keys before the end of the range count; the sub-tile
+  // is never the first, so m is set and a fully masked one changes nothing)
+  auto redo_exact = [&](const f32x16 (&S)[2], u32x4 (&P)[2][2], float (&lt)[2], int64_t key0,
+                        auto tail_tag) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       float rmax = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, S[qb][r]);
+      for (int r = 0; r < 16; ++r) {
+        float x = S[qb][r];
+        if constexpr (decltype(tail_tag)::value) {
+          if (key0 + 16 * (r >> 3) + 8 * hf + (r & 7) >= tr.k_end) x = -INFINITY;
+        }
+        rmax = fmaxf(rmax, x);
+      }
       rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
       const float mx = __builtin_fmaf(rmax, qscale, -m[qb]);
       const float delta = mset[qb] ? fmaxf(mx, 0.f) : mx;
@@ -448,7 +464,7 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
       lsum[qb] *= factor;
       o[qb][0] *= factor;
       o[qb][1] *= factor;
-      lt[qb] = exp_pack(qb, S[qb], 0.f, P[qb], 0, std::false_type{});
+      lt[qb] = exp_pack(qb, S[qb], 0.f, P[qb], key0, tail_tag);
     }
   };
 
@@ -478,27 +494,26 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
   __syncthreads();
   // fast pipeline step: QK -> Sn (stage stK, sub sbK), PV of Pp (stage stV,
   // sub sbV), softmax Sc -> Pc of the full sub-tile in stage stC, sub sbC
-  auto step = [&](int stK, int sbK, int stV, int sbV, int stC, int sbC, const f32x16 (&Sc)[2],
-                  u32x4 (&Pc)[2][2], f32x16 (&Sn)[2], const u32x4 (&Pp)[2][2])
-      __attribute__((always_inline)) {
+  // (tail: the same with the sub-tile's keys starting at key0 masked at the
+  // end of the range)
+  auto step_m = [&](int stK, int sbK, int stV, int sbV, int stC, int sbC, const f32x16 (&Sc)[2],
+                    u32x4 (&Pc)[2][2], f32x16 (&Sn)[2], const u32x4 (&Pp)[2][2], int64_t key0,
+                    auto tail_tag) __attribute__((always_inline)) {
     float lt[2];
-    step_fast(stK, sbK, stV, sbV, Sc, Pc, Sn, Pp, lt);
+    step_fast(stK, sbK, stV, sbV, Sc, Pc, Sn, Pp, lt, key0, tail_tag);
     if (__any(!(lt[0] <= kRescaleSum && lt[1] <= kRescaleSum))) {
       // rare: recompute this sub-tile's scores (its tile is still in LDS)
       f32x16 Sr[2];
       qk(stC, sbC, Sr);
-      redo_exact(Sr, Pc, lt);
+      redo_exact(Sr, Pc, lt, key0, tail_tag);
     }
     lsum[0] += lt[0];
     lsum[1] += lt[1];
   };
-  // the same step in plain order, masking the sub-tile at key0 (tail tile)
-  auto step_tail = [&](int stK, int sbK, int stV, int sbV, const f32x16 (&Sc)[2],
-                       u32x4 (&Pc)[2][2], f32x16 (&Sn)[2], const u32x4 (&Pp)[2][2], int64_t key0)
+  auto step = [&](int stK, int sbK, int stV, int sbV, int stC, int sbC, const f32x16 (&Sc)[2],
+                  u32x4 (&Pc)[2][2], f32x16 (&Sn)[2], const u32x4 (&Pp)[2][2])
       __attribute__((always_inline)) {
-    qk(stK, sbK, Sn);
-    pv(stV, sbV, Pp);
-    softmax(Sc, Pc, false, key0, std::true_type{});
+    step_m(stK, sbK, stV, sbV, stC, sbC, Sc, Pc, Sn, Pp, 0, std::false_type{});
   };
   // tile t+1 must have landed before its first QK; tile t+2 then loads into
   // the stage of tile t-1
@@ -514,10 +529,10 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
   if (has_tail) {
     qk(0, 1, Sb);
     softmax(Sa, Pa, true, key00, std::true_type{});
-    step_tail(0, 2, 0, 0, Sb, Pb, Sa, Pa, key00 + 32);
-    step_tail(0, 3, 0, 1, Sa, Pa, Sb, Pb, key00 + 64);
+    step_m(0, 2, 0, 0, 0, 1, Sb, Pb, Sa, Pa, key00 + 32, std::true_type{});
+    step_m(0, 3, 0, 1, 0, 2, Sa, Pa, Sb, Pb, key00 + 64, std::true_type{});
     if (ntiles > 1) advance(0, kStages - 1);
-    step_tail(st1, 0, 0, 2, Sb, Pb, Sa, Pa, key00 + 96);
+    step_m(st1, 0, 0, 2, 0, 3, Sb, Pb, Sa, Pa, key00 + 96, std::true_type{});
   } else {
     qk(0, 1, Sb);
     softmax(Sa, Pa, true, key00, std::false_type{});
