@@ -76,3 +76,15 @@ def test_projection_flops():
     assert bench.flops_linear(137400, 1024, 3072) == 2 * 137400 * 1024 * 3072
     # the QKV projection is three output projections' worth of work
     assert bench.flops_linear(7, 64, 192) == 3 * bench.flops_linear(7, 64, 64)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the timed path runs on one device; more ranks stop before any GPU call
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300, cwd=root)
+    assert r.returncode == 2
+    assert "exactly one GPU" in r.stderr
+    assert r.stdout == ""
