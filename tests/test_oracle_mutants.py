@@ -52,6 +52,13 @@ MUTANTS = [
     ("linear_bias_by_row", "elem(b, dtype, n)", "elem(b, dtype, m % N)"),
     ("qkv_k_v_swapped", "k[m * C + c] = y[m * 3 * C + C + c];",
      "k[m * C + c] = y[m * 3 * C + 2 * C + c];"),
+    ("softmax_not_normalised", "out[(r * H + h) * d + e] = acc[e] / wsum;",
+     "out[(r * H + h) * d + e] = acc[e];"),
+    ("mean_column_outside_denominator", "wsum += w;\n        if (col[c] >= 0) {",
+     "if (col[c] >= 0) {\n          wsum += w;"),
+    ("frame_misses_last_key", "for (int64_t j = f0; j < f0 + L; ++j) col[nc++] = j;",
+     "for (int64_t j = f0; j < f0 + L - 1; ++j) col[nc++] = j;"),
+    ("keep_idx_without_frame_offset", "int64_t t = (int64_t)f * L + u;", "int64_t t = u;"),
 ]
 
 
