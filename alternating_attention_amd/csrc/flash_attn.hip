@@ -41,12 +41,17 @@
 //
 // Softmax: the MFMA produces exact fp32 dot products of the bf16 rows; one
 // FMA per score turns them into log2 units and subtracts the row's
-// reference max m.  m is updated lazily: the first sub-tile, or a sub-tile
-// whose probabilities sum above 2^16 in a lane, takes a wave-uniform slow
-// path that (re)computes its scores, raises m to the sub-tile max and
-// rescales O and l (the textbook online softmax); every other sub-tile uses
-// P = exp2(S - m) as is.  P is rounded to bf16 (RNE) for the PV MFMA; l
-// (summed from the rounded P) and O accumulate in fp32.
+// reference max m, the exact max of the first sub-tile (online softmax with
+// the reference fixed early: the sums need m only as a common shift, and the
+// first sub-tile's max keeps every later P = exp2(S - m) finite unless a
+// score exceeds it by 128 in log2 units).  P is rounded to bf16 (RNE) for
+// the PV MFMA; O accumulates in fp32, and so do the row sums of the rounded
+// P, on the matrix core (a 16x16x32 MFMA against a 0/1 operand; see rowsum).
+// The step keeps no per-step max test: after the key loop every wave checks
+// that its row sums and output accumulators are finite, and if any wave of
+// the workgroup finds otherwise, all redo their rows with the exact online
+// softmax one sub-tile at a time (max update, rescale of O and l), where
+// every P is at most 1.
 //
 // fp32 path: a plain VALU kernel (one lane per query and head, exact online
 // softmax in fp32), used for fp32 inputs.
@@ -69,7 +74,6 @@ constexpr int kQPerWave = 64;
 constexpr int kBQ = 8 * kQPerWave;     // queries per workgroup
 constexpr int kBK = 128;               // keys per LDS tile (4 sub-tiles of 32)
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleSum = 65536.f;  // lazy-rescale trigger (2^16)
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -80,6 +84,17 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   p[0] = (__bf16)lo;
   p[1] = (__bf16)hi;
   return __builtin_bit_cast(uint32_t, p);
+}
+
+// The same conversion (v_cvt_pk_bf16_f32 rounds to nearest even, S0 into
+// the low half) as one instruction placed where it stands, right after the
+// exps that produce its operands, with the one wait state their results
+// need.  Left to itself the compiler gathers four such conversions into a
+// group once all four pairs exist, which serialises the step's end.
+__device__ __forceinline__ uint32_t pack_bf16_now(float lo, float hi) {
+  uint32_t r;
+  asm("s_nop 0\n\tv_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+  return r;
 }
 
 // LDS row of key (within a 32-key sub-tile) swaps bits 2 and 3.
@@ -93,6 +108,15 @@ struct TileRange {
   int64_t k_begin, k_end;    // key rows
   int32_t head;
 };
+
+// A workgroup-uniform 64-bit value, stated as such: the 64-bit divisions
+// that derive the tile bounds run on the VALU, and without this the results
+// would stay in vector registers for the whole kernel.
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 // Workgroups are dispatched round-robin over the 8 XCDs (block b runs on
 // XCD b % 8), each with its own L2.  Logical tile order gives every XCD one
@@ -159,8 +183,14 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 template <KeyRange KR>
 __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) {
   __shared__ __attribute__((aligned(16))) char lds[kStages][kStage];
+  __shared__ int fallback;  // set when some wave's rows need the exact loop
 
-  const TileRange tr = tile_range<KR>(p);
+  TileRange tr = tile_range<KR>(p);
+  tr.q_begin = uniform64(tr.q_begin);
+  tr.q_end = uniform64(tr.q_end);
+  tr.k_begin = uniform64(tr.k_begin);
+  tr.k_end = uniform64(tr.k_end);
+  tr.head = (int32_t)__builtin_amdgcn_readfirstlane((uint32_t)tr.head);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -187,10 +217,13 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
 
   // ---- softmax state.  Lane (l32, hf) of block qb holds, for its query:
   // o[qb][db] register r = O^T[d][q] with d = 32*db + 8*(r/4) + 4*hf + r%4;
-  // lsum = this lane's share of the row sum; m = reference max (log2 units).
+  // m = reference max (log2 units).  Row sums: in the main loop, lrs[qb]
+  // (a 16x16 MFMA accumulator, see rowsum below); in the exact fallback
+  // loop, lsum[qb] = this lane's share of the row sum.
   f32x16 o[2][2];
   float lsum[2], m[2];
   bool mset[2];
+  f32x4 lrs[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     o[qb][0] = 0.f;
@@ -198,7 +231,9 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
     lsum[qb] = 0.f;
     m[qb] = 0.f;
     mset[qb] = false;
+    lrs[qb] = 0.f;
   }
+  if (tid == 0) fallback = 0;  // published by the first barrier below
 
   // ---- DMA plan: wave w issues the tile's 1 KB instructions w, w+8, ...
   // (0..17: K, 18..37: V).  A lane's granule: key offset within the tile and
@@ -214,14 +249,6 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
       col = gc < 8 ? gc * 16 : 0;
     }
   };
-  uint32_t dma_off[kDmaSlots];
-#pragma unroll
-  for (int s = 0; s < kDmaSlots; ++s) {
-    int key;
-    uint32_t col;
-    dma_granule(8 * s + wave, key, col);
-    dma_off[s] = (uint32_t)key * (uint32_t)row_bytes + col;
-  }
   const char* kbytes = (const char*)p.k + (int64_t)head * 128;
   const char* vbytes = (const char*)p.v + (int64_t)head * 128;
   // Issue the DMA of the tile at key0 into `stage`; with clamp (the ragged
@@ -243,7 +270,12 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
         key = key < tr.k_end ? key : tr.k_end - 1;
         src = base + key * row_bytes + col;
       } else {
-        src = base + key0 * row_bytes + dma_off[s];
+        // the lane's granule, recomputed per tile (a few integer ops; kept
+        // in registers across the loop it would cost ten of them)
+        int kk;
+        uint32_t col;
+        dma_granule(i, kk, col);
+        src = base + key0 * row_bytes + ((uint32_t)kk * (uint32_t)row_bytes + col);
       }
       char* dst = &lds[stage][isk ? i * 1024 : kKTile + (i - kKInstr) * 1024];
       // Issued from asm: the compiler then does not make every later LDS
@@ -266,10 +298,38 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
   const int g16 = lane >> 4, j16 = lane & 15;
   const int vread = kKTile + (8 * hf + (j16 >> 2)) * kVRow + (16 * (g16 & 1) + 4 * (j16 & 3)) * 2;
 
+  // keys of the sub-tile at key0 that lie before the end of the range, as a
+  // uniform count in [0, 32]: a key at offset j of the sub-tile is masked
+  // iff j >= valid(key0)
+  auto valid = [&](int64_t key0) __attribute__((always_inline)) {
+    const int64_t n = tr.k_end - key0;
+    return (int)__builtin_amdgcn_readfirstlane((uint32_t)(n < 0 ? 0 : n > 32 ? 32 : n));
+  };
   const int64_t nkeys = tr.k_end - tr.k_begin;
-  const int64_t nfull = nkeys / kBK;
-  const int64_t ntiles = (nkeys + kBK - 1) / kBK;
+  const int64_t nfull = uniform64(nkeys / kBK);
+  const int64_t ntiles = uniform64((nkeys + kBK - 1) / kBK);
   const bf16x2 kOnes = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+
+  // Row sums on the matrix core: D += A B with v_mfma_f32_16x16x32_bf16,
+  // B = one P operand register set as it stands (lane L gives column L%16,
+  // k-group L/16), A = 0/1 selecting k-groups {0, 2} for rows 0-7 and
+  // {1, 3} for rows 8-15.  Lane L of a P operand holds query L%32, so
+  // k-groups 0 and 2 are query j = L%16 and groups 1 and 3 query 16 + j:
+  // rows 0-7 of column j sum the 16 probabilities of query j, rows 8-15
+  // those of query 16 + j.  Accumulator lane L (rows 4*(L/16)..+3 of column
+  // L%16) thus holds the running sum of query L (L < 16), L - 16 (L < 48) or
+  // L - 32.  This keeps the row sum off the VALU, whose dot2 form competes
+  // with the MFMA issue far more than its instruction count suggests.
+  bf16x8 rs_sel;
+  {
+    const uint32_t w = (((g16 & 1) == 0) == (j16 < 8)) ? 0x3f803f80u : 0u;
+    const u32x4 wv = {w, w, w, w};
+    rs_sel = __builtin_bit_cast(bf16x8, wv);
+  }
+  auto rowsum = [&](int qb, const u32x4& P) __attribute__((always_inline)) {
+    lrs[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rs_sel, __builtin_bit_cast(bf16x8, P),
+                                                     lrs[qb], 0, 0, 0);
+  };
 
   // ---- building blocks on one 32-key sub-tile (sb of the tile in stage st)
   // S^T (raw dot products) of both query blocks
@@ -301,13 +361,14 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
               va, __builtin_bit_cast(bf16x8, P[qb][c2]), o[qb][db], 0, 0, 0);
       }
   };
-  // P = exp2(qscale*S - m - delta) rounded to bf16 into the PV operand;
-  // returns the lane's fp32 sum of the rounded P.  Tail: keys at or past the
-  // end of the range get P = 0.
-  auto exp_pack = [&](int qb, const f32x16& S, float delta, u32x4 (&P)[2], int64_t key0,
-                      auto tail_tag) __attribute__((always_inline)) {
+  // P = exp2(qscale*S - m) rounded to bf16 into the PV operand.  Tail: keys
+  // at or past the end of the range get P = 0.  With_sum: also returns the
+  // lane's fp32 sum of the rounded P (exact fallback loop only).
+  auto exp_pack = [&](int qb, const f32x16& S, u32x4 (&P)[2], int64_t key0, auto tail_tag,
+                      auto sum_tag) __attribute__((always_inline)) {
     constexpr bool tail = decltype(tail_tag)::value;
-    const float nm = -(m[qb] + delta);
+    constexpr bool with_sum = decltype(sum_tag)::value;
+    const float nm = -m[qb];
     float acc = 0.f;
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2)
@@ -316,165 +377,148 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
         float z0 = __builtin_fmaf(S[8 * c2 + 2 * e], qscale, nm);
         float z1 = __builtin_fmaf(S[8 * c2 + 2 * e + 1], qscale, nm);
         if constexpr (tail) {
-          const int64_t k0 = key0 + 16 * c2 + 8 * hf + 2 * e;
-          if (k0 >= tr.k_end) z0 = -INFINITY;
-          if (k0 + 1 >= tr.k_end) z1 = -INFINITY;
+          const int j = 16 * c2 + 8 * hf + 2 * e, lim = valid(key0);
+          if (j >= lim) z0 = -INFINITY;
+          if (j + 1 >= lim) z1 = -INFINITY;
         }
         const uint32_t pp = pack_bf16(__builtin_amdgcn_exp2f(z0), __builtin_amdgcn_exp2f(z1));
         P[c2][e] = pp;
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), kOnes, acc, false);
+        if constexpr (with_sum)
+          acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), kOnes, acc, false);
       }
     return acc;
   };
-  // Softmax of one sub-tile: the fast path uses the reference max m as is;
-  // the first sub-tile, or one whose probabilities sum above 2^16 in a lane,
-  // raises m to the sub-tile max (and rescales O and l) and redoes P.
-  auto softmax = [&](const f32x16 (&S)[2], u32x4 (&P)[2][2], bool first, int64_t key0,
-                     auto tail_tag) __attribute__((always_inline)) {
-    float lt[2] = {0.f, 0.f};
-    bool slow = first;
-    if (!slow) {
-      lt[0] = exp_pack(0, S[0], 0.f, P[0], key0, tail_tag);
-      lt[1] = exp_pack(1, S[1], 0.f, P[1], key0, tail_tag);
-      slow = __any(!(lt[0] <= kRescaleSum && lt[1] <= kRescaleSum));
-    }
-    if (slow) {
+  // The sub-tile's max over its keys (tail: keys before the end of the
+  // range only), across both lane halves, in raw dot-product units.
+  auto subtile_max = [&](const f32x16& S, int64_t key0, auto tail_tag)
+      __attribute__((always_inline)) {
+    float rmax = -INFINITY;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float rmax = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = S[qb][r];
-          if constexpr (decltype(tail_tag)::value) {
-            const int64_t key = key0 + 16 * (r >> 3) + 8 * hf + (r & 7);
-            if (key >= tr.k_end) x = -INFINITY;
-          }
-          rmax = fmaxf(rmax, x);
-        }
-        rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
-        const float mx = rmax == -INFINITY ? -INFINITY : __builtin_fmaf(rmax, qscale, -m[qb]);
-        // a fully masked sub-tile (tail) leaves the state unchanged
-        const float delta = mx == -INFINITY ? 0.f : (mset[qb] ? fmaxf(mx, 0.f) : mx);
-        const float factor = mset[qb] ? exp2f(-delta) : 1.f;
-        m[qb] += delta;
-        mset[qb] = mset[qb] || mx != -INFINITY;
-        lsum[qb] *= factor;
-        o[qb][0] *= factor;
-        o[qb][1] *= factor;
-        lt[qb] = exp_pack(qb, S[qb], 0.f, P[qb], key0, tail_tag);
+    for (int r = 0; r < 16; ++r) {
+      float x = S[r];
+      if constexpr (decltype(tail_tag)::value) {
+        if (16 * (r >> 3) + 8 * hf + (r & 7) >= valid(key0)) x = -INFINITY;
       }
+      rmax = fmaxf(rmax, x);
     }
-    lsum[0] += lt[0];
-    lsum[1] += lt[1];
+    return fmaxf(rmax, __shfl_xor(rmax, 32));
   };
-
-  // Steady-state step, fast path, unit by unit: QK of the next sub-tile
-  // (K at stK/sbK) and PV of the previous one (V at stV/sbV, operand Pp)
-  // on the matrix core, each MFMA followed by one pair of this sub-tile's
-  // softmax (scores Sc -> Pc); the sched barriers pin that order.  Returns
-  // the lane sums of the rounded P in lt.  Tail: the sub-tile's keys start
-  // at key0 and those at or past the end of the range get P = 0.
-  auto step_fast = [&](int stK, int sbK, int stV, int sbV, const f32x16 (&Sc)[2],
-                       u32x4 (&Pc)[2][2], f32x16 (&Sn)[2], const u32x4 (&Pp)[2][2],
-                       float (&lt)[2], int64_t key0, auto tail_tag) __attribute__((always_inline)) {
-    constexpr bool tail = decltype(tail_tag)::value;
-    const char* sk = &lds[stK][0] + kread + sbK * 32 * kKRow;
-    const char* sv = &lds[stV][0] + vread + sbV * 32 * kVRow;
-    // PV units first (they free Pp), then the QK units (they fill Sn); the
-    // operand of each MFMA pair is read from LDS two units ahead
-    bf16x8 va[2][2], ka[4];
-    auto load_v = [&](int db, int c2) __attribute__((always_inline)) {
-      const char* a = sv + 16 * c2 * kVRow + db * 64;
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a);
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a + 4 * kVRow));
-      va[db][c2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
-    auto load_k = [&](int c) __attribute__((always_inline)) {
-      ka[c] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(sk + c * 32));
-    };
-    const float nm0 = -m[0], nm1 = -m[1];
-    lt[0] = 0.f;
-    lt[1] = 0.f;
-    auto pair = [&](int u) __attribute__((always_inline)) {
-      const int qb = u >> 3, c2 = (u >> 2) & 1, e = u & 3;
-      const float nm = qb ? nm1 : nm0;
-      float z0 = __builtin_fmaf(Sc[qb][8 * c2 + 2 * e], qscale, nm);
-      float z1 = __builtin_fmaf(Sc[qb][8 * c2 + 2 * e + 1], qscale, nm);
-      if constexpr (tail) {
-        const int64_t k0 = key0 + 16 * c2 + 8 * hf + 2 * e;
-        if (k0 >= tr.k_end) z0 = -INFINITY;
-        if (k0 + 1 >= tr.k_end) z1 = -INFINITY;
-      }
-      const uint32_t pp = pack_bf16(__builtin_amdgcn_exp2f(z0), __builtin_amdgcn_exp2f(z1));
-      Pc[qb][c2][e] = pp;
-      lt[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), kOnes, lt[qb],
-                                               false);
-    };
-    load_v(0, 0);
-    load_v(0, 1);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      // PV unit: operand (db, c2) for query block qb
-      const int db = u >> 2, c2 = (u >> 1) & 1, qb = u & 1;
-      if (u == 1) load_v(1, 0);
-      if (u == 3) load_v(1, 1);
-      if (u == 5) load_k(0);
-      if (u == 6) load_k(1);
-      pair(u);
-      o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          va[db][c2], __builtin_bit_cast(bf16x8, Pp[qb][c2]), o[qb][db], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int u = 8; u < 16; ++u) {
-      // QK unit: k-step c for query block qb
-      const int w = u - 8, c = w >> 1, qb = w & 1;
-      if (w == 1) load_k(2);
-      if (w == 3) load_k(3);
-      pair(u);
-      Sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qreg[qb][c],
-                                                       c == 0 ? f32x16(0.f) : Sn[qb], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  // the rare exact redo after a fast step: raise m to the sub-tile max
-  // (O and l rescaled) and recompute P
-  // (tail: only the keys before the end of the range count; the sub-tile
-  // is never the first, so m is set and a fully masked one changes nothing)
-  auto redo_exact = [&](const f32x16 (&S)[2], u32x4 (&P)[2][2], float (&lt)[2], int64_t key0,
-                        auto tail_tag) __attribute__((always_inline)) {
+  // Exact online-softmax update of one sub-tile (the textbook form): raise
+  // m to the sub-tile max, rescale O and l, then P and its row sum.  A fully
+  // masked sub-tile (tail) leaves the state unchanged.
+  auto softmax_exact = [&](const f32x16 (&S)[2], u32x4 (&P)[2][2], int64_t key0, auto tail_tag)
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float rmax = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = S[qb][r];
-        if constexpr (decltype(tail_tag)::value) {
-          if (key0 + 16 * (r >> 3) + 8 * hf + (r & 7) >= tr.k_end) x = -INFINITY;
-        }
-        rmax = fmaxf(rmax, x);
-      }
-      rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
-      const float mx = __builtin_fmaf(rmax, qscale, -m[qb]);
-      const float delta = mset[qb] ? fmaxf(mx, 0.f) : mx;
+      const float rmax = subtile_max(S[qb], key0, tail_tag);
+      const float mx = rmax == -INFINITY ? -INFINITY : __builtin_fmaf(rmax, qscale, -m[qb]);
+      const float delta = mx == -INFINITY ? 0.f : (mset[qb] ? fmaxf(mx, 0.f) : mx);
       const float factor = mset[qb] ? exp2f(-delta) : 1.f;
       m[qb] += delta;
-      mset[qb] = true;
+      mset[qb] = mset[qb] || mx != -INFINITY;
       lsum[qb] *= factor;
       o[qb][0] *= factor;
       o[qb][1] *= factor;
-      lt[qb] = exp_pack(qb, S[qb], 0.f, P[qb], key0, tail_tag);
+      lsum[qb] += exp_pack(qb, S[qb], P[qb], key0, tail_tag, std::true_type{});
     }
   };
 
-  // ---- software pipeline over 32-key sub-tiles j (four per LDS tile): step
-  // j runs QK of sub-tile j+1 and PV of sub-tile j-1 on the matrix core
-  // while the VALU computes the softmax of sub-tile j.  Three LDS stages:
-  // tile t+2 loads into the stage of tile t-1, whose last reader (the PV of
-  // its last sub-tile) ran before the barrier that precedes the load.
-  f32x16 Sa[2], Sb[2];
-  u32x4 Pa[2][2], Pb[2][2];
+  // ---- the pipeline's state: one score tile S[qb] and one probability
+  // operand set P[qb] per query block, the K operands of one sub-tile (ka)
+  // and the V operands of one (va)
+  f32x16 S[2];
+  u32x4 P[2][2];
+  bf16x8 ka[4], va[2][2];
+  auto load_k = [&](int st, int sb, int c) __attribute__((always_inline)) {
+    ka[c] = __builtin_bit_cast(
+        bf16x8, *(const lds_u32x4*)(&lds[st][0] + kread + sb * 32 * kKRow + c * 32));
+  };
+  // V^T operand (db, c2) of a sub-tile: two transposed reads
+  auto load_v = [&](int st, int sb, int db, int c2) __attribute__((always_inline)) {
+    const char* a = &lds[st][0] + vread + sb * 32 * kVRow + 16 * c2 * kVRow + db * 64;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a);
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a + 4 * kVRow));
+    va[db][c2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+
+  // Step j (the softmax of sub-tile j), sixteen units of one MFMA and one
+  // pair of scores each, pinned in that order by sched barriers:
+  //   units  0-3   QK(j, block 1)        | softmax(j, block 0), pairs 0-3
+  //   units  4-7   PV(j-1, block 1)      | softmax(j, block 0), pairs 4-7
+  //   units  8-11  QK(j+1, block 0)      | softmax(j, block 1), pairs 0-3
+  //   units 12-15  PV(j, block 0)        | softmax(j, block 1), pairs 4-7
+  // so every MFMA's operands were produced at least four units earlier and
+  // each block needs one score tile and one probability set: block 0's S
+  // is consumed (units 0-7) before QK(j+1) refills it (8-11), block 1's P
+  // is consumed by PV(j-1) (4-7) before the softmax rewrites it (8-15).
+  // The K operands of sub-tile j+1 (at stK/sbK) load in units 4-7, after
+  // QK(j, block 1) last read ka; the V operands of sub-tile j (at stV/sbV)
+  // in units 8-11, after PV(j-1) last read va.  The row sums of each P set
+  // go to the matrix core beside its PV products.  First (sub-tile 0): no
+  // PV(j-1), and block 1's reference max is taken at unit 8, once its
+  // scores exist.  Tail: keys at or past the end of the range get P = 0.
+  auto step = [&](int stK, int sbK, int stV, int sbV, int64_t key0, auto first_tag,
+                  auto tail_tag) __attribute__((always_inline)) {
+    constexpr bool first = decltype(first_tag)::value;
+    constexpr bool tail = decltype(tail_tag)::value;
+    const int lim = tail ? valid(key0) : 32;
+    // softmax of pair w (operand half w/4, register pair w%4) of block qb:
+    // z = scale*S - m (log2 units), P = exp2(z) as bf16
+    auto pair = [&](int qb, int w) __attribute__((always_inline)) {
+      const int c2 = w >> 2, e = w & 3;
+      const float nm = -m[qb];
+      float z0 = __builtin_fmaf(S[qb][8 * c2 + 2 * e], qscale, nm);
+      float z1 = __builtin_fmaf(S[qb][8 * c2 + 2 * e + 1], qscale, nm);
+      if constexpr (tail) {
+        const int j = 16 * c2 + 8 * hf + 2 * e;
+        if (j >= lim) z0 = -INFINITY;
+        if (j + 1 >= lim) z1 = -INFINITY;
+      }
+      P[qb][c2][e] = pack_bf16_now(__builtin_amdgcn_exp2f(z0), __builtin_amdgcn_exp2f(z1));
+    };
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (u >= 4 && u < 8) load_k(stK, sbK, u - 4);
+      // V operands in the order the PV units use them: (db, c2) = (0,0),
+      // (1,0), (0,1), (1,1), so consecutive PV MFMAs alternate accumulators
+      if (u >= 8 && u < 12) load_v(stV, sbV, (u - 8) & 1, (u - 8) >> 1);
+      if (first && u == 8) {
+        m[1] = subtile_max(S[1], key0, tail_tag) * qscale;
+        mset[1] = true;
+      }
+      pair(u >> 3, u & 7);
+      if (u < 4) {
+        S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[u], qreg[1][u],
+                                                       u == 0 ? f32x16(0.f) : S[1], 0, 0, 0);
+      } else if (u < 8) {
+        if constexpr (!first) {
+          const int db = (u - 4) & 1, c2 = (u - 4) >> 1;
+          o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              va[db][c2], __builtin_bit_cast(bf16x8, P[1][c2]), o[1][db], 0, 0, 0);
+          if (db == 0) rowsum(1, P[1][c2]);
+        }
+      } else if (u < 12) {
+        const int c = u - 8;
+        S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qreg[0][c],
+                                                       c == 0 ? f32x16(0.f) : S[0], 0, 0, 0);
+      } else {
+        const int db = (u - 12) & 1, c2 = (u - 12) >> 1;
+        o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            va[db][c2], __builtin_bit_cast(bf16x8, P[0][c2]), o[0][db], 0, 0, 0);
+        if (db == 0) rowsum(0, P[0][c2]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- main loop over 32-key sub-tiles j, four per LDS tile.  Three LDS
+  // stages: tile t+2 loads into the stage of tile t-1 at the barrier before
+  // step 4t+3 (the first step that reads tile t+1); tile t-1's last reader
+  // (the V loads of step 4t-1) ran before it.  The reference max m is the
+  // exact max of the first sub-tile; later sub-tiles use P = exp2(S - m) as
+  // is, which stays finite unless a score exceeds m by 128 (log2 units) --
+  // checked after the loop.
   // Tile order: the ragged tail first (if any), then the full tiles; the
   // softmax sums do not depend on the key order.
   const bool has_tail = ntiles > nfull;
@@ -492,54 +536,40 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
   if (ntiles > 1) issue_tile(1, 1);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  // fast pipeline step: QK -> Sn (stage stK, sub sbK), PV of Pp (stage stV,
-  // sub sbV), softmax Sc -> Pc of the full sub-tile in stage stC, sub sbC
-  // (tail: the same with the sub-tile's keys starting at key0 masked at the
-  // end of the range)
-  auto step_m = [&](int stK, int sbK, int stV, int sbV, int stC, int sbC, const f32x16 (&Sc)[2],
-                    u32x4 (&Pc)[2][2], f32x16 (&Sn)[2], const u32x4 (&Pp)[2][2], int64_t key0,
-                    auto tail_tag) __attribute__((always_inline)) {
-    float lt[2];
-    step_fast(stK, sbK, stV, sbV, Sc, Pc, Sn, Pp, lt, key0, tail_tag);
-    if (__any(!(lt[0] <= kRescaleSum && lt[1] <= kRescaleSum))) {
-      // rare: recompute this sub-tile's scores (its tile is still in LDS)
-      f32x16 Sr[2];
-      qk(stC, sbC, Sr);
-      redo_exact(Sr, Pc, lt, key0, tail_tag);
-    }
-    lsum[0] += lt[0];
-    lsum[1] += lt[1];
-  };
-  auto step = [&](int stK, int sbK, int stV, int sbV, int stC, int sbC, const f32x16 (&Sc)[2],
-                  u32x4 (&Pc)[2][2], f32x16 (&Sn)[2], const u32x4 (&Pp)[2][2])
-      __attribute__((always_inline)) {
-    step_m(stK, sbK, stV, sbV, stC, sbC, Sc, Pc, Sn, Pp, 0, std::false_type{});
-  };
-  // tile t+1 must have landed before its first QK; tile t+2 then loads into
-  // the stage of tile t-1
   auto advance = [&](int64_t t, int st_prev) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     if (t + 2 < ntiles) issue_tile(t + 2, st_prev);
   };
-  // ---- tile 0 (the ragged tail when there is one): steps 0..3
+  // ---- tile 0 (the ragged tail when there is one): steps 0..3.  Before
+  // step 0: K operands and block 0's scores of sub-tile 0, and block 0's
+  // reference max (sub-tile 0 holds at least one key).
   const int64_t key00 = tile_key0(0);
-  const int st1 = ntiles > 1 ? 1 : 0;  // QK target of step 3 (a dummy re-read if no tile 1)
-  qk(0, 0, Sa);
+  const int st1 = ntiles > 1 ? 1 : 0;  // K source of step 3 (a dummy re-read if no tile 1)
+#pragma unroll
+  for (int c = 0; c < 4; ++c) load_k(0, 0, c);
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qreg[0][c], c == 0 ? f32x16(0.f) : S[0],
+                                                   0, 0, 0);
+  constexpr std::true_type yes{};
+  constexpr std::false_type no{};
   if (has_tail) {
-    qk(0, 1, Sb);
-    softmax(Sa, Pa, true, key00, std::true_type{});
-    step_m(0, 2, 0, 0, 0, 1, Sb, Pb, Sa, Pa, key00 + 32, std::true_type{});
-    step_m(0, 3, 0, 1, 0, 2, Sa, Pa, Sb, Pb, key00 + 64, std::true_type{});
+    m[0] = subtile_max(S[0], key00, yes) * qscale;
+    mset[0] = true;
+    step(0, 1, 0, 0, key00, yes, yes);
+    step(0, 2, 0, 1, key00 + 32, no, yes);
+    step(0, 3, 0, 2, key00 + 64, no, yes);
     if (ntiles > 1) advance(0, kStages - 1);
-    step_m(st1, 0, 0, 2, 0, 3, Sb, Pb, Sa, Pa, key00 + 96, std::true_type{});
+    step(st1, 0, 0, 3, key00 + 96, no, yes);
   } else {
-    qk(0, 1, Sb);
-    softmax(Sa, Pa, true, key00, std::false_type{});
-    step(0, 2, 0, 0, 0, 1, Sb, Pb, Sa, Pa);
-    step(0, 3, 0, 1, 0, 2, Sa, Pa, Sb, Pb);
+    m[0] = subtile_max(S[0], key00, no) * qscale;
+    mset[0] = true;
+    step(0, 1, 0, 0, 0, yes, no);
+    step(0, 2, 0, 1, 0, no, no);
+    step(0, 3, 0, 2, 0, no, no);
     if (ntiles > 1) advance(0, kStages - 1);
-    step(st1, 0, 0, 2, 0, 3, Sb, Pb, Sa, Pa);
+    step(st1, 0, 0, 3, 0, no, no);
   }
   // ---- full tiles 1 .. ntiles-1: steps 4t .. 4t+3
   int st = 0;
@@ -548,14 +578,75 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
     st = st == kStages - 1 ? 0 : st + 1;
     const int st_next = st == kStages - 1 ? 0 : st + 1;
     const bool has_next = t + 1 < ntiles;
-    step(st, 1, st_prev, 3, st, 0, Sa, Pa, Sb, Pb);  // QK(t,1) | PV(t-1,3) | softmax(t,0)
-    step(st, 2, st, 0, st, 1, Sb, Pb, Sa, Pa);       // QK(t,2) | PV(t,0)   | softmax(t,1)
-    step(st, 3, st, 1, st, 2, Sa, Pa, Sb, Pb);       // QK(t,3) | PV(t,1)   | softmax(t,2)
+    step(st, 1, st, 0, 0, no, no);
+    step(st, 2, st, 1, 0, no, no);
+    step(st, 3, st, 2, 0, no, no);
     if (has_next) advance(t, st_prev);
-    // QK(t+1,0) | PV(t,2) | softmax(t,3); the QK re-reads this tile when t is last
-    step(has_next ? st_next : st, 0, st, 2, st, 3, Sb, Pb, Sa, Pa);
+    // K of sub-tile 4t+4 (tile t+1); a dummy re-read of this tile when t is last
+    step(has_next ? st_next : st, 0, st, 3, 0, no, no);
   }
-  pv(st, 3, Pb);  // drain
+  // drain: PV and row sums of the last sub-tile's block 1
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) {
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+      o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          va[db][c2], __builtin_bit_cast(bf16x8, P[1][c2]), o[1][db], 0, 0, 0);
+    rowsum(1, P[1][c2]);
+  }
+
+  // Row sums into the lane of their query (lane L holds query L % 32):
+  // accumulator lane L % 32 (< 16) or L % 32 + 16 (>= 16) has it.
+  const int rs_src = l32 < 16 ? l32 : l32 + 16;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float full = __shfl(lrs[qb][0], rs_src);
+    lsum[qb] = hf == 0 ? full : 0.f;
+  }
+
+  // ---- the check: every row sum and output accumulator finite (x * 0 is
+  // NaN exactly for x non-finite); otherwise a score exceeded m by 128 or
+  // more somewhere in the workgroup, and every wave redoes its rows with
+  // the exact online softmax (P <= 1 throughout).
+  {
+    float nf = lsum[0] * 0.f + lsum[1] * 0.f;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) nf = __builtin_fmaf(o[qb][db][r], 0.f, nf);
+    if (__any(nf != nf) && lane == 0) fallback = 1;
+  }
+  __syncthreads();
+  if (fallback) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      o[qb][0] = 0.f;
+      o[qb][1] = 0.f;
+      lsum[qb] = 0.f;
+      m[qb] = 0.f;
+      mset[qb] = false;
+    }
+    // one tile at a time through stage 0, each sub-tile exact
+    for (int64_t t = 0; t < ntiles; ++t) {
+      __syncthreads();  // every wave is done with stage 0
+      issue_tile(t, 0);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      const int64_t key0 = tile_key0(t);
+      for (int sb = 0; sb < 4; ++sb) {
+        f32x16 Sx[2];
+        u32x4 Px[2][2];
+        qk(0, sb, Sx);
+        if (has_tail && t == 0)
+          softmax_exact(Sx, Px, key0 + 32 * sb, std::true_type{});
+        else
+          softmax_exact(Sx, Px, 0, std::false_type{});
+        pv(0, sb, Px);
+      }
+    }
+  }
 
   // This wave's first query row, recomputed here: the value from the Q load
   // would otherwise be kept, in registers or scratch, across the loop.
