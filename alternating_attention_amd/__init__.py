@@ -135,6 +135,11 @@ class Sga:
         return CSga(self.stride_h, self.stride_w, self.phase_h, self.phase_w,
                     int(self.diagonal), int(self.mean_fill))
 
+    @classmethod
+    def from_c(cls, cs: CSga) -> "Sga":
+        return cls(int(cs.stride_h), int(cs.stride_w), int(cs.phase_h), int(cs.phase_w),
+                   bool(cs.diagonal), int(cs.mean_fill))
+
 
 def _load():
     if not os.path.exists(LIB_PATH):
@@ -424,13 +429,20 @@ def sga_attn_rows(q_rows, k, v, frames: Frames, sga: Sga, row_begin: int, out=No
     return out, workspace
 
 
+def _plan(arr, n):
+    """(mode, Sga or None) per slot: the SGA parameters only for SGA slots."""
+    return [(int(arr[i].mode), Sga.from_c(arr[i].sga) if arr[i].mode == MODE_SGA else None)
+            for i in range(n)]
+
+
 def layer_schedule(num_global: int, num_early: int, sga: Sga | None):
-    """Per-global-slot list of (mode, CSga) of the training-free pipeline."""
+    """Per-global-slot list of (mode, Sga or None) of the training-free
+    pipeline; each entry can be passed to ``attention`` as it stands."""
     arr = (CLayer * max(num_global, 1))()
     cs = sga.c() if sga is not None else None
     _check(lib.vga_layer_schedule(num_global, num_early,
                                   ctypes.byref(cs) if cs is not None else None, arr))
-    return [(arr[i].mode, arr[i].sga) for i in range(num_global)]
+    return _plan(arr, num_global)
 
 
 def layer_schedule_sga(num_global: int, num_early: int, per_slot):
@@ -443,7 +455,7 @@ def layer_schedule_sga(num_global: int, num_early: int, per_slot):
     if len(per_slot) != max(n, 0):
         raise ValueError("need %d per-slot SGA parameters, got %d" % (max(n, 0), len(per_slot)))
     _check(lib.vga_layer_schedule_sga(num_global, num_early, sg, arr))
-    return [(arr[i].mode, arr[i].sga) for i in range(num_global)]
+    return _plan(arr, num_global)
 
 
 def layer_schedule_register(num_global: int, num_early: int, register_every: int,
@@ -454,7 +466,7 @@ def layer_schedule_register(num_global: int, num_early: int, register_every: int
     cs = sga.c() if sga is not None else None
     _check(lib.vga_layer_schedule_register(num_global, num_early, register_every,
                                            ctypes.byref(cs) if cs is not None else None, arr))
-    return [(arr[i].mode, arr[i].sga) for i in range(num_global)]
+    return _plan(arr, num_global)
 
 
 def _prepare_linear(x, w, b, frames: Frames, n_out: int):
@@ -509,7 +521,11 @@ def out_proj(o, w, b, frames: Frames, out=None):
 
 def attention(mode: int, q, k, v, frames: Frames, sga: Sga | None = None, out=None,
               workspace=None):
-    """Dispatch one layer by schedule mode; returns the output tensor."""
+    """Run one layer of a schedule: ``mode`` and ``sga`` as one entry of
+    ``layer_schedule*`` returns them.  Returns the output tensor; the SGA
+    and register workspaces are allocated here unless passed."""
+    if mode == MODE_SGA and sga is None:
+        raise ValueError("an SGA layer needs its Sga parameters")
     if mode == MODE_FRAME:
         return frame_attn(q, k, v, frames, out)
     if mode == MODE_GLOBAL:

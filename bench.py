@@ -361,11 +361,12 @@ def run(args):
                 "(phase 1, diagonal, mean-fill); exact global layer timed once beside it")
 
         def step():
-            for mode, cs in vga.layer_schedule(24, 8, sga):
-                if mode == vga.MODE_FRAME:
-                    timed("frame", lambda: vga.frame_attn(q, k, v, frames, out))
-                else:
-                    timed("sga", lambda: vga.sga_attn(q, k, v, frames, sga, out_b, ws))
+            # each slot through the schedule dispatch, as a trunk would run it
+            for mode, p in vga.layer_schedule(24, 8, sga):
+                name = "frame" if mode == vga.MODE_FRAME else "sga"
+                dst = out if mode == vga.MODE_FRAME else out_b
+                timed(name, lambda mode=mode, p=p, dst=dst:
+                      vga.attention(mode, q, k, v, frames, p, dst, ws))
         work = {"frame": 8 * flops_frame(N, L, H), "sga": 16 * flops_sga(T, nk, H)}
         dominant, modes, sgas = "sga", ["frame"], [sga]
         step_counts = [8, 16]
@@ -381,18 +382,13 @@ def run(args):
                 "layers (phase 0), 8 SGA 3x3 layers (phase 1), all with diagonal and "
                 "mean-fill; exact global layer timed once beside it")
 
-        def as_sga(cs):
-            return vga.Sga(cs.stride_h, cs.stride_w, cs.phase_h, cs.phase_w, bool(cs.diagonal),
-                           cs.mean_fill)
-
         def step():
-            for mode, cs in vga.layer_schedule_sga(24, 8, ramp):
+            for mode, p in vga.layer_schedule_sga(24, 8, ramp):
                 if mode == vga.MODE_FRAME:
-                    timed("frame", lambda: vga.frame_attn(q, k, v, frames, out))
+                    timed("frame", lambda: vga.attention(mode, q, k, v, frames, None, out))
                 else:
-                    p = as_sga(cs)
                     timed("sga_%dx%d" % (p.stride_h, p.stride_w),
-                          lambda p=p: vga.sga_attn(q, k, v, frames, p, out_b, ws))
+                          lambda p=p: vga.attention(vga.MODE_SGA, q, k, v, frames, p, out_b, ws))
         work = {"frame": 8 * flops_frame(N, L, H),
                 "sga_2x2": 8 * flops_sga(T, int(lays[(2, 2)].num_kept), H),
                 "sga_3x3": 8 * flops_sga(T, int(lays[(3, 3)].num_kept), H)}

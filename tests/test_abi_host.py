@@ -283,6 +283,18 @@ def test_layer_schedule(vga):
         vga.layer_schedule(4, 1, vga.Sga(stride_h=0))
     assert vga.lib.vga_layer_schedule(3, 1, None, None) == 1
     assert vga.layer_schedule(0, 0, None) == []
+    # entries go to attention() as they stand: Sga parameters on SGA slots only
+    sch = vga.layer_schedule(4, 1, vga.Sga(2, 2, 0, 0, True, 2))
+    assert sch[0] == (vga.MODE_FRAME, None)
+    assert all(e == (vga.MODE_SGA, vga.Sga(2, 2, 0, 0, True, 2)) for e in sch[1:])
+    assert all(p is None for _, p in vga.layer_schedule(3, 1, None))
+
+
+def test_attention_dispatch_refuses_sga_without_parameters(vga):
+    with pytest.raises(ValueError):
+        vga.attention(vga.MODE_SGA, None, None, None, vga.Frames(1, 2, 2, 0, 1))
+    with pytest.raises(ValueError):
+        vga.attention(7, None, None, None, vga.Frames(1, 2, 2, 0, 1))
 
 
 def test_layer_schedule_per_slot_sga(vga):
