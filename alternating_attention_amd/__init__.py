@@ -8,6 +8,8 @@ C names without the ``vga_`` prefix:
 * ``frame_attn(q, k, v, frames)``  -> vga_frame_attn
 * ``global_attn(q, k, v, frames)`` -> vga_global_attn
 * ``sga_attn(q, k, v, frames, sga)`` -> vga_sga_attn (+ workspace)
+* ``sga_attn_noalloc(q, k, v, frames, sga)`` -> vga_sga_attn_noalloc (no
+  workspace argument: the library's static scratch, 64 MiB per GPU)
 * ``sga_select(k, v, frames, sga)`` -> vga_sga_select (the selection,
   compaction and dropped mean alone; returns the workspace)
 * ``sga_workspace_layout(frames, sga)`` -> vga_sga_workspace_layout
@@ -48,7 +50,7 @@ EXPORTS = ["vga_frame_attn", "vga_global_attn", "vga_sga_workspace_layout",
            "vga_sga_attn", "vga_register_workspace_layout", "vga_register_attn",
            "vga_layer_schedule", "vga_layer_schedule_register", "vga_layer_schedule_sga",
            "vga_frame_attn_rows", "vga_global_attn_rows", "vga_sga_attn_rows",
-           "vga_sga_select",
+           "vga_sga_select", "vga_sga_attn_noalloc",
            "vga_qkv_proj", "vga_out_proj",
            "vga_status_string", "vga_last_error", "vga_abi_version"]
 
@@ -157,6 +159,9 @@ def _load():
     lib.vga_sga_attn.restype = ctypes.c_int
     lib.vga_sga_attn.argtypes = [ctypes.POINTER(CFrames), ctypes.POINTER(CSga), vp, vp, vp,
                                  vp, vp, ctypes.c_size_t, vp]
+    lib.vga_sga_attn_noalloc.restype = ctypes.c_int
+    lib.vga_sga_attn_noalloc.argtypes = [ctypes.POINTER(CFrames), ctypes.POINTER(CSga), vp, vp,
+                                         vp, vp, vp]
     lib.vga_sga_select.restype = ctypes.c_int
     lib.vga_sga_select.argtypes = [ctypes.POINTER(CFrames), ctypes.POINTER(CSga), vp, vp, vp,
                                    ctypes.c_size_t, vp]
@@ -297,6 +302,19 @@ def sga_attn(q, k, v, frames: Frames, sga: Sga, out=None, workspace=None):
                             v.data_ptr(), out.data_ptr(), workspace.data_ptr(),
                             workspace.numel(), _stream(q.device)))
     return out, workspace
+
+
+def sga_attn_noalloc(q, k, v, frames: Frames, sga: Sga, out=None):
+    """Subsampled Global Attention with the library's static scratch as the
+    workspace (nothing allocated by the call; calls that overlap on one GPU
+    race).  Returns out."""
+    out = _prepare(q, k, v, frames, out)
+    cf = frames.c(_dtype_code(q))
+    cs = sga.c()
+    _check(lib.vga_sga_attn_noalloc(ctypes.byref(cf), ctypes.byref(cs), q.data_ptr(),
+                                    k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                    _stream(q.device)))
+    return out
 
 
 def sga_select(k, v, frames: Frames, sga: Sga, workspace=None):

@@ -8,8 +8,18 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/vga.h"
 #include "vga_internal.h"
+
+// The workspace of vga_sga_attn_noalloc: one static array per GPU, held
+// from the first call on that GPU until the process ends.  Host code never
+// passes this name to a kernel or a copy (on the host it only stands for
+// the device symbol); it uses the device address that hipGetSymbolAddress
+// returns for the current device (scratch_for below).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -408,6 +418,45 @@ vga_status linear_run(const vga_frames* s, const void* x, const void* w, const v
   return finish(vga::launch_linear(s->dtype == VGA_BF16, p, hs), hs, what);
 }
 
+// The device address of `scratch` on the device that runs `stream` (the
+// current device for the null stream), taken once per device with that
+// device current and kept.  The table is shared by all threads.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+vga_status scratch_for(hipStream_t hs, void** out) {
+  int dev = 0;
+  hipError_t e = hs ? hipStreamGetDevice(hs, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(VGA_ERR_HIP, "vga_sga_attn_noalloc: device of the stream: %s",
+                hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(VGA_ERR_UNSUPPORTED, "vga_sga_attn_noalloc: device %d beyond the first %d", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    if (e != hipSuccess)
+      return fail(VGA_ERR_HIP, "vga_sga_attn_noalloc: select device %d: %s", dev,
+                  hipGetErrorString(e));
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess || !ptr)
+      return fail(VGA_ERR_HIP, "vga_sga_attn_noalloc: scratch address on device %d: %s", dev,
+                  hipGetErrorString(e));
+    if (back != hipSuccess)
+      return fail(VGA_ERR_HIP, "vga_sga_attn_noalloc: restore device %d: %s", cur,
+                  hipGetErrorString(back));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return VGA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -468,6 +517,29 @@ vga_status vga_sga_attn(const vga_frames* shape, const vga_sga* sga, const void*
                         size_t workspace_bytes, void* stream) {
   return sga_run(shape, sga, 0, 0, false, q, k, v, o, workspace, workspace_bytes, stream,
                  "vga_sga_attn");
+}
+
+vga_status vga_sga_attn_noalloc(const vga_frames* shape, const vga_sga* sga, const void* q,
+                                const void* k, const void* v, void* o, void* stream) {
+  // the size check needs no device: a call beyond the scratch fails here
+  Checked c;
+  vga_status st = check_shape(shape, &c);
+  if (st != VGA_OK) return st;
+  vga_sga r;
+  st = resolve_sga(shape, sga, &r);
+  if (st != VGA_OK) return st;
+  vga_sga_ws_layout w;
+  fill_layout(shape, c, make_grid(shape, r), &w);
+  if (w.total > kScratchBytes)
+    return fail(VGA_ERR_WORKSPACE,
+                "vga_sga_attn_noalloc: needs %llu bytes of workspace, the static scratch holds "
+                "%llu; use vga_sga_attn with a caller workspace",
+                (unsigned long long)w.total, (unsigned long long)kScratchBytes);
+  void* ws = nullptr;
+  st = scratch_for((hipStream_t)stream, &ws);
+  if (st != VGA_OK) return st;
+  return sga_run(shape, sga, 0, 0, false, q, k, v, o, ws, kScratchBytes, stream,
+                 "vga_sga_attn_noalloc");
 }
 
 vga_status vga_sga_select(const vga_frames* shape, const vga_sga* sga, const void* k,

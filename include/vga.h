@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define VGA_ABI_VERSION 5
+#define VGA_ABI_VERSION 6
 
 typedef enum {
   VGA_OK = 0,
@@ -253,6 +253,28 @@ vga_status vga_sga_attn_rows(const vga_frames* shape, const vga_sga* sga, int64_
                              int64_t row_end, const void* q_rows, const void* k,
                              const void* v, void* o_rows, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* vga_sga_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same kernels and the same
+ * result as vga_sga_attn, with the workspace in a static device array of
+ * the library, VGA_SGA_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, which each
+ * GPU that runs the call holds from its first call until the process ends.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); its first call on a device takes the array's device address
+ * (hipGetSymbolAddress, with that device current) and keeps it.  The
+ * device is the one that runs `stream` (the current device for NULL).
+ * Every section of the workspace is written by the call before it is read,
+ * so nothing carries over between calls, but all calls on one GPU share
+ * the array: calls that overlap in time on one GPU (other streams, other
+ * threads) race and must not be issued.  Arguments as vga_sga_attn.
+ * Errors: as vga_sga_attn; VGA_ERR_WORKSPACE (checked before any device
+ * call) when the layout of vga_sga_workspace_layout needs more than the
+ * scratch holds (at 16 heads of bf16: about 44 frames of 37x37+5 tokens at
+ * stride 2x2, 109 at 3x3). */
+#define VGA_SGA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+vga_status vga_sga_attn_noalloc(const vga_frames* shape, const vga_sga* sga, const void* q,
+                                const void* k, const void* v, void* o, void* stream);
 
 /* The projections around an attention layer ("VGGT CVPR25 Best Paper"
  * notes, section "Alternating-Attention": the frame and global blocks are

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(vga):
 
 
 def test_abi_version_and_strings(vga):
-    assert vga.abi_version() == 5
+    assert vga.abi_version() == 6
     for code, name in enumerate(vga.STATUS_NAMES):
         assert vga.status_string(code) == name
 
@@ -332,3 +332,21 @@ def test_schedule_matches_oracle(vga):
     with pytest.raises(vga.VgaError) as ei:
         vga.layer_schedule_register(4, 0, -1, None)
     assert ei.value.status == 4
+
+
+def test_sga_noalloc_refuses_beyond_scratch(vga):
+    # the workspace of 100 frames at stride 2x2 (about 150 MB) exceeds the
+    # 64 MiB static scratch: refused before any device call (so this runs
+    # without a GPU), with the sizes in the message
+    big = vga.Frames(num_frames=100, grid_h=37, grid_w=37, num_special=5, num_heads=16)
+    cf, cs = big.c(vga.VGA_BF16), vga.Sga(2, 2, 0, 0).c()
+    lay = vga.sga_workspace_layout(big, vga.Sga(2, 2, 0, 0))
+    assert lay.total > 64 << 20
+    st = vga.lib.vga_sga_attn_noalloc(ctypes.byref(cf), ctypes.byref(cs), None, None, None,
+                                      None, None)
+    assert st == 7, vga.last_error()
+    assert "static scratch holds 67108864" in vga.last_error()
+    # a bad stride is still a parameter error, as for vga_sga_attn
+    bad = vga.Sga(0, 2, 0, 0).c()
+    assert vga.lib.vga_sga_attn_noalloc(ctypes.byref(cf), ctypes.byref(bad), None, None, None,
+                                        None, None) == 4
