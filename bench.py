@@ -11,6 +11,10 @@ layer (key selection, gather + mean, attention).  The default workload is
                     [--workload n100|n300|n800|n800reg|shard8|sweep]
 
 Prints ONE JSON line.  `value` is tokens/s through one step (T / step time).
+With the default workload the line also carries, measured after the timed
+steps, the 300- and 800-frame comparisons ("n300", "n800"): one exact global
+layer against one SGA layer (2x2 at 300 frames, 3x3 at 800), with the frame
+layer and the 24-slot AVGGT schedule at 800 frames (--no-extras skips them).
 Other workloads:
   n300    -- one exact global layer vs one SGA 2x2 layer at 300 frames
              (speedup, output deviation);
@@ -671,7 +675,88 @@ def run(args):
             w, frames, sgas, modes, qkv, args.cpu_rows,
             row_range=(3 * T // 8, 4 * T // 8) if args.workload == "shard8" else None,
             proj=proj, counts=step_counts)
+    if args.workload == "n100" and not args.no_extras:
+        # the 300- and 800-frame comparisons of exact global attention with
+        # SGA, after the timed step (not part of it)
+        del q, k, v, out, out_b, ws
+        torch.cuda.empty_cache()
+        result["n300"] = speedup_record(vga, torch, "n300", vga.Sga(2, 2, 0, 0, True, True),
+                                        with_frame=False)
+        result["n800"] = speedup_record(vga, torch, "n800", vga.Sga(3, 3, 1, 1, True, True),
+                                        with_frame=True)
     return result
+
+
+def speedup_record(vga, torch, wname, sga, with_frame, reps=3):
+    """One exact global layer (timed once, on the kernels already warm from
+    the main workload) against the SGA layer (median of `reps` calls) on the
+    seeded shifted-feature-field inputs of `wname`; with_frame: the frame
+    layer too and the 24-slot AVGGT schedule (8 frame + 16 SGA) from the
+    layer times.  Output deviation of SGA from exact attention, both from
+    the GPU."""
+    import vga_inputs
+    w = vga_inputs.WORKLOADS[wname]
+    dev = torch.device("cuda", 0)
+    frames = vga.Frames(w.num_frames, w.grid_h, w.grid_w, w.num_special, w.num_heads)
+    T, H, N, L = frames.tokens, frames.num_heads, frames.num_frames, frames.tokens_per_frame
+    log("extra %s: generating inputs (T=%d)" % (wname, T))
+    q, k, v = vga_inputs.feature_field_qkv(N, w.grid_h, w.grid_w, w.num_special, H, HEAD_DIM,
+                                           seed=w.seed, device=dev)
+    out, out_b = torch.empty_like(q), torch.empty_like(q)
+    lay = vga.sga_workspace_layout(frames, sga)
+    ws = torch.empty(int(lay.total), dtype=torch.uint8, device=dev)
+    nk = int(lay.num_kept)
+    torch.cuda.synchronize()
+
+    def timed_calls(fn, n):
+        t = Timer(torch)
+        for _ in range(n):
+            with t:
+                fn()
+        torch.cuda.synchronize()
+        return t.ms()
+
+    log("extra %s: SGA %dx%d layer x%d" % (wname, sga.stride_h, sga.stride_w, reps + 1))
+    sga_ms = timed_calls(lambda: vga.sga_attn(q, k, v, frames, sga, out_b, ws), reps + 1)[1:]
+    log("extra %s: exact global layer, once" % wname)
+    g_ms = timed_calls(lambda: vga.global_attn(q, k, v, frames, out), 1)[0]
+    t_sga = float(np.median(sga_ms))
+    fg, fs = flops_global(T, H), flops_sga(T, nk, H)
+    d = (out_b.float() - out.float())
+    rec = {
+        "workload": "N=%d frames x %d tokens = %d tokens, %d heads x 64, bf16; exact global "
+                    "layer vs SGA %dx%d (phase %d, diagonal, count-weighted mean-fill)" % (
+                        N, L, T, H, sga.stride_h, sga.stride_w, sga.phase_h),
+        "global": {"ms": g_ms, "tflops": fg / (g_ms * 1e-3) / 1e12,
+                   "frac_mfma_peak": fg / (g_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                   "tokens_per_s": T / (g_ms * 1e-3), "calls": 1},
+        "sga": {"ms": t_sga, "ms_all": sga_ms, "tflops": fs / (t_sga * 1e-3) / 1e12,
+                "frac_mfma_peak": fs / (t_sga * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                "tokens_per_s": T / (t_sga * 1e-3), "kept_per_frame": int(lay.kept_per_frame),
+                "note": "whole call: selection, gather, mean and attention"},
+        "sga_vs_exact_layer_speedup": g_ms / t_sga,
+        "ideal_speedup_from_work": fg / fs,
+        "sga_deviation": {"max_abs": float(d.abs().max()), "mean_abs": float(d.abs().mean()),
+                          "rel_l2": float(d.norm() / out.float().norm())},
+    }
+    del d
+    if with_frame:
+        log("extra %s: frame layer x%d" % (wname, reps + 1))
+        f_ms = float(np.median(timed_calls(lambda: vga.frame_attn(q, k, v, frames, out),
+                                           reps + 1)[1:]))
+        ff = flops_frame(N, L, H)
+        rec["frame"] = {"ms": f_ms, "tflops": ff / (f_ms * 1e-3) / 1e12,
+                        "frac_mfma_peak": ff / (f_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        sched = 8 * f_ms + 16 * t_sga
+        rec["schedule_24_slots"] = {
+            "avggt_8frame_16sga_ms": sched, "exact_24_global_ms": 24 * g_ms,
+            "speedup": 24 * g_ms / sched,
+            "ideal_speedup_from_work": 24 * fg / (8 * ff + 16 * fs),
+            "plan": [m for m, _ in vga.layer_schedule(24, 8, sga)] == [vga.MODE_FRAME] * 8
+            + [vga.MODE_SGA] * 16}
+    del q, k, v, out, out_b, ws
+    torch.cuda.empty_cache()
+    return rec
 
 
 def copy_probe():
@@ -702,6 +787,8 @@ def main():
     ap.add_argument("--no-gpu-state", action="store_true",
                     help="skip the amd-smi power and clock samples (for runs under a profiler)")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="n100 only: skip the 300- and 800-frame exact-vs-SGA records")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the multi-GPU sharding of this path is a "
