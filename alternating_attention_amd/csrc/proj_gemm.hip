@@ -148,11 +148,16 @@ __global__ void __launch_bounds__(kThreads, 1) linear_bf16_kernel(LinearParams p
   }
 
   issue(0, 0);
-  // this tile's bias (zero past N or without a bias), read once
+  // this tile's bias (zero past N or without a bias), read once, element
+  // by element: the bias need only be aligned to its 2-byte element
   if (tid < kBN / 8) {
     u32x4 bw = {0u, 0u, 0u, 0u};
     const int64_t n = n0 + 8 * tid;
-    if (p.b && n < p.N) bw = *(const u32x4*)((const uint16_t*)p.b + n);
+    if (p.b && n < p.N) {
+      const uint16_t* bs = (const uint16_t*)p.b + n;   // N is a multiple of 64
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bw[e] = (uint32_t)bs[2 * e] | ((uint32_t)bs[2 * e + 1] << 16);
+    }
     *(__attribute__((address_space(3))) u32x4*)&bias_s[8 * tid] = bw;
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);

@@ -395,6 +395,30 @@ def test_projections(vga, shape, dt):
         check_linear(host(y), ry, dt, "out", ay, C)
 
 
+def test_projection_bias_element_aligned_bf16(vga):
+    # the ABI asks the bias to be aligned to its element only: a bf16 bias
+    # starting 2 bytes past a 16-byte boundary gives the same result as an
+    # aligned copy of it (and the oracle's)
+    frames = vga.Frames(3, 7, 9, 3, 2)
+    T, C = frames.tokens, 128
+    rng = np.random.default_rng(811)
+    x = rng.standard_normal((T, C)).astype(np.float32)
+    w = (rng.standard_normal((3 * C, C)) / math.sqrt(C)).astype(np.float32)
+    b = rng.standard_normal(3 * C + 1).astype(np.float32)
+    xd, wd, bfull = to_dev((x, w, b), torch.bfloat16)
+    bshift = bfull[1:]                        # data_ptr 2 bytes past the allocation
+    assert bshift.data_ptr() % 16 == 2 and bshift.is_contiguous()
+    baligned = bshift.clone()
+    say("case proj-bias-offset bf16")
+    got = vga.qkv_proj(xd, wd, bshift, frames)
+    ref_gpu = vga.qkv_proj(xd, wd, baligned, frames)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.qkv_proj(host(xd), host(wd), host(baligned), 2)
+    for g, r, ro in zip(got, ref_gpu, (rq, rk, rv)):
+        assert torch.equal(g, r)
+        check_linear(host(g), ro, "bf16", "qkv, bias at +2 bytes")
+
+
 @pytest.mark.parametrize("dt,H", [("bf16", 64), ("f32", 32)])
 def test_projections_most_heads(vga, dt, H):
     # the widest rows the ABI accepts: C = 4096 (bf16, W_qkv 12,288 x 4,096)
