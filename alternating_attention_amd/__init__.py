@@ -36,7 +36,9 @@ import os
 from dataclasses import dataclass
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libvga.so")
+# VGA_LIB_PATH loads another build of the same library (the CPU tests use it
+# for the build whose host code carries AddressSanitizer and UBSan)
+LIB_PATH = os.environ.get("VGA_LIB_PATH") or os.path.join(_HERE, "libvga.so")
 
 VGA_OK = 0
 STATUS_NAMES = ["VGA_OK", "VGA_ERR_NULL", "VGA_ERR_SHAPE", "VGA_ERR_DTYPE",

@@ -47,5 +47,54 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host code built with AddressSanitizer and UBSan for CPU-side checks of the
+# argument validation, workspace layouts and schedules (the device code is
+# compiled as usual: every sanitizer flag is host-only).  The library links
+# the shared clang sanitizer runtime, which the process that loads it must
+# preload (sanitizer_runtime()).
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer"]
+SANITIZED_LIB = os.path.join(ROOT, "_build", "asan", "libvga.so")
+
+
+def sanitizer_runtime() -> str:
+    """Path of the shared clang AddressSanitizer runtime to LD_PRELOAD."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "lib", "llvm", "bin",
+                         "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/lib/llvm/bin/clang"
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True, check=True)
+    return r.stdout.strip()
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """libvga.so with sanitized host code, into _build/asan/ (CPU tests only)."""
+    build_dir = os.path.join(ROOT, "_build", "asan")
+    os.makedirs(build_dir, exist_ok=True)
+
+    def one(src):
+        obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+        cmd = ([HIPCC, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON
+               + DEVICE_FLAGS + SANITIZE_HOST)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
+        return obj
+
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(one, SOURCES))
+    cmd = ([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", SANITIZED_LIB] + objs
+           + ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+              "-shared-libasan"])
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
+    if verbose:
+        print("built", SANITIZED_LIB)
+    return SANITIZED_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)

@@ -37,7 +37,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "vga_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "libvga_oracle.so")
+# VGA_ORACLE_LIB loads another build of vga_oracle.c (the sanitizer build
+# of build_sanitized, in the CPU tests)
+_LIB_PATH = os.environ.get("VGA_ORACLE_LIB") or os.path.join(_HERE, "libvga_oracle.so")
 
 MODE_FRAME, MODE_GLOBAL, MODE_SGA, MODE_REGISTER = 0, 1, 2, 3
 _F32, _BF16 = 0, 1
@@ -52,6 +54,22 @@ def build(force: bool = True) -> str:
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
+
+
+def build_sanitized(out: str) -> str:
+    """vga_oracle.c with gcc's AddressSanitizer and UBSan into `out`; the
+    loading process must preload gcc's libasan (sanitizer_runtime())."""
+    cmd = ["gcc", "-O1", "-g", "-std=c99", "-fopenmp", "-fPIC", "-shared",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-fno-omit-frame-pointer", _SRC, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def sanitizer_runtime() -> str:
+    r = subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True, text=True,
+                       check=True)
+    return r.stdout.strip()
 
 
 _lib = None
