@@ -26,7 +26,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGatherThreads = 256;
-constexpr int kUnroll = 8;          // tokens in flight per thread
+constexpr int kUnroll = 16;         // tokens in flight per thread
 constexpr int kMaxTokensPerBlock = 2048;
 
 // Rank of token t among the kept tokens, or -1 when it is dropped.

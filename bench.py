@@ -501,14 +501,27 @@ def run(args):
         per["sga"]["gather_bytes"] = gb
         per["sga"]["kept_per_frame"] = int(lay.kept_per_frame)
         # the selection, gather and mean alone (the HBM-bound part of the SGA
-        # call), timed after the steps on the same inputs and workspace
+        # call), timed after the steps on the same inputs and workspace: 20
+        # calls queued back to back between two events give the device time
+        # per call (both launches and the gap between them).  A call timed
+        # alone on an idle stream also counts the host's launch latency; its
+        # median is reported beside it.
+        n_sel = 20
+        vga.sga_select(k, v, frames, sga, ws)
         sel = Timer(torch)
+        with sel:
+            for _ in range(n_sel):
+                vga.sga_select(k, v, frames, sga, ws)
+        one = Timer(torch)
         for _ in range(10):
-            with sel:
+            torch.cuda.synchronize()
+            with one:
                 vga.sga_select(k, v, frames, sga, ws)
         torch.cuda.synchronize()
-        sms = float(np.median(sel.ms()))
+        sms = float(sel.ms()[0]) / n_sel
         per["sga_select"] = {"ms_per_call": sms, "calls_per_step": 0.0,
+                             "timing": "%d calls back to back" % n_sel,
+                             "ms_single_call_median": float(np.median(one.ms())),
                              "gb_per_s": gb / (sms * 1e-3) / 1e9,
                              "frac_hbm_peak": gb / (sms * 1e-3) / 1e9 / PEAK_HBM_GBS}
         att = per["sga"]["ms_per_call"] - sms
