@@ -193,7 +193,8 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
   tr.head = (int32_t)__builtin_amdgcn_readfirstlane((uint32_t)tr.head);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // uniform: the DMA slot choices below become scalar branches
+  const int wave = (int)__builtin_amdgcn_readfirstlane((uint32_t)tid >> 6);
   const int l32 = lane & 31;
   const int hf = lane >> 5;  // lane half: k-group of the MFMA operands
   const int H = p.H;
@@ -306,8 +307,10 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
     return (int)__builtin_amdgcn_readfirstlane((uint32_t)(n < 0 ? 0 : n > 32 ? 32 : n));
   };
   const int64_t nkeys = tr.k_end - tr.k_begin;
-  const int64_t nfull = uniform64(nkeys / kBK);
-  const int64_t ntiles = uniform64((nkeys + kBK - 1) / kBK);
+  // tile counts (uniform; below 2^24 since keys number below 2^31)
+  const int32_t nfull = (int32_t)__builtin_amdgcn_readfirstlane((uint32_t)(nkeys / kBK));
+  const int32_t ntiles =
+      (int32_t)__builtin_amdgcn_readfirstlane((uint32_t)((nkeys + kBK - 1) / kBK));
   const bf16x2 kOnes = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 
   // Row sums on the matrix core: D += A B with v_mfma_f32_16x16x32_bf16,
@@ -522,11 +525,12 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
   // Tile order: the ragged tail first (if any), then the full tiles; the
   // softmax sums do not depend on the key order.
   const bool has_tail = ntiles > nfull;
-  auto tile_key0 = [&](int64_t i) __attribute__((always_inline)) {
-    return has_tail ? (i == 0 ? tr.k_begin + nfull * kBK : tr.k_begin + (i - 1) * kBK)
-                    : tr.k_begin + i * kBK;
+  auto tile_key0 = [&](int32_t i) __attribute__((always_inline)) {
+    return has_tail ? (i == 0 ? tr.k_begin + (int64_t)nfull * kBK
+                              : tr.k_begin + (int64_t)(i - 1) * kBK)
+                    : tr.k_begin + (int64_t)i * kBK;
   };
-  auto issue_tile = [&](int64_t i, int st) __attribute__((always_inline)) {
+  auto issue_tile = [&](int32_t i, int st) __attribute__((always_inline)) {
     if (has_tail && i == 0)
       issue(tile_key0(0), st, std::true_type{});
     else
@@ -536,7 +540,7 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
   if (ntiles > 1) issue_tile(1, 1);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  auto advance = [&](int64_t t, int st_prev) __attribute__((always_inline)) {
+  auto advance = [&](int32_t t, int st_prev) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     if (t + 2 < ntiles) issue_tile(t + 2, st_prev);
@@ -573,7 +577,7 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
   }
   // ---- full tiles 1 .. ntiles-1: steps 4t .. 4t+3
   int st = 0;
-  for (int64_t t = 1; t < ntiles; ++t) {
+  for (int32_t t = 1; t < ntiles; ++t) {
     const int st_prev = st;
     st = st == kStages - 1 ? 0 : st + 1;
     const int st_next = st == kStages - 1 ? 0 : st + 1;
@@ -629,7 +633,7 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
       mset[qb] = false;
     }
     // one tile at a time through stage 0, each sub-tile exact
-    for (int64_t t = 0; t < ntiles; ++t) {
+    for (int32_t t = 0; t < ntiles; ++t) {
       __syncthreads();  // every wave is done with stage 0
       issue_tile(t, 0);
       __builtin_amdgcn_s_waitcnt(0x0F70);
