@@ -66,6 +66,7 @@ def test_schedule_plans_through_attention(vga):
                for a in tiny_qkv(frames.tokens, 2, 64, seed=77))
     qh, kh, vh = bits(q), bits(k), bits(v)
     plans = {
+        "avggt 24 slots": vga.layer_schedule(24, 8, vga.Sga(3, 3, 1, 1)),
         "avggt 3x3": vga.layer_schedule(6, 2, vga.Sga(3, 3, -1, -1)),
         "frame + exact": vga.layer_schedule(5, 2, None),
         "per-slot strides": vga.layer_schedule_sga(
