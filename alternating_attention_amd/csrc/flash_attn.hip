@@ -479,6 +479,13 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
       }
       P[qb][c2][e] = pack_bf16_now(__builtin_amdgcn_exp2f(z0), __builtin_amdgcn_exp2f(z1));
     };
+    // The two waves of a SIMD (w and w+4) take turns at the higher issue
+    // priority, step by step.  Left to the arbiter, the older wave runs
+    // ahead and waits about a quarter of each tile at the barrier.
+    if ((sbV & 1) == (wave >> 2))
+      __builtin_amdgcn_s_setprio(1);
+    else
+      __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
