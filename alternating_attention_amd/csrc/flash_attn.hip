@@ -122,31 +122,35 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
 // XCD b % 8), each with its own L2.  Logical tile order gives every XCD one
 // contiguous range, so the query tiles that share a frame's or a head's K/V
 // run on the same XCD at about the same time.
-__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t nblocks) {
-  constexpr int64_t kXcds = 8;
-  const int64_t q = nblocks / kXcds, r = nblocks % kXcds;
-  const int64_t x = b % kXcds;
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nblocks) {
+  constexpr uint32_t kXcds = 8;
+  const uint32_t q = nblocks / kXcds, r = nblocks % kXcds;
+  const uint32_t x = b % kXcds;
   return x * q + min(x, r) + b / kXcds;
 }
 
+// The workgroup's tile range.  Block, frame and tile counts are below 2^31
+// (T < 2^31), so the index arithmetic runs in 32 bits: 64-bit divisions
+// here cost about 2 % of a frame-attention workgroup.
 template <KeyRange KR>
 __device__ __forceinline__ TileRange tile_range(const FlashParams& p) {
   TileRange t;
-  const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
+  const uint32_t b = xcd_remap(blockIdx.x, gridDim.x);
   if constexpr (KR == KeyRange::kFrame) {
-    const int64_t qtpf = (p.L + kBQ - 1) / kBQ;
-    const int64_t per_head = qtpf * p.num_frames;
-    t.head = (int32_t)(b / per_head);
-    const int64_t rem = b % per_head;
-    const int64_t f = rem / qtpf, qt = rem % qtpf;
-    t.q_begin = f * p.L + qt * kBQ;
-    t.q_end = min(t.q_begin + kBQ, (f + 1) * (int64_t)p.L);
-    t.k_begin = f * p.L;
-    t.k_end = (f + 1) * (int64_t)p.L;
+    const uint32_t qtpf = ((uint32_t)p.L + kBQ - 1) / kBQ;
+    const uint32_t per_head = qtpf * (uint32_t)p.num_frames;
+    const uint32_t head = b / per_head, rem = b - head * per_head;
+    const uint32_t f = rem / qtpf, qt = rem - f * qtpf;
+    t.head = (int32_t)head;
+    t.k_begin = (int64_t)f * p.L;
+    t.k_end = t.k_begin + p.L;
+    t.q_begin = t.k_begin + (int64_t)qt * kBQ;
+    t.q_end = min(t.q_begin + kBQ, t.k_end);
   } else {
-    const int64_t nqt = (p.num_q + kBQ - 1) / kBQ;
-    t.head = (int32_t)(b / nqt);
-    t.q_begin = (b % nqt) * kBQ;
+    const uint32_t nqt = (uint32_t)((p.num_q + kBQ - 1) / kBQ);
+    const uint32_t head = b / nqt;
+    t.head = (int32_t)head;
+    t.q_begin = (int64_t)(b - head * nqt) * kBQ;
     t.q_end = min(t.q_begin + kBQ, p.num_q);
     t.k_begin = 0;
     t.k_end = p.num_keys;
