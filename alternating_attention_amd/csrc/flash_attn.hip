@@ -166,17 +166,23 @@ __device__ __forceinline__ bool sga_kept(const SgaGrid& g, int64_t t) {
   return (r % g.sh == g.oh) && (c % g.sw == g.ow);
 }
 
-// LDS tiles.  K: 128 rows of 128 bytes padded to 144 (row i of a 32-key
-// sub-tile holds key perm_row(i)); V: 128 rows (natural key order) padded to
-// 160 bytes.  The padding spreads the rows that one LDS read touches over
-// distinct banks, and keeps every read address a per-lane base plus an
-// immediate.  Both tiles are filled by global_load_lds_dwordx4 (global ->
-// LDS without registers), 1 KB (64 x 16 bytes) per instruction; granules
-// that fall in the padding load a harmless in-range duplicate.
-constexpr int kKRow = 144, kVRow = 160;
-constexpr int kKTile = kBK * kKRow, kVTile = kBK * kVRow;     // 18432, 20480
-constexpr int kStage = kKTile + kVTile;                        // 38912
-constexpr int kKInstr = kKTile / 1024, kVInstr = kVTile / 1024;  // 18, 20
+// LDS tiles (the LDS has 64 four-byte banks).
+//  K: 128 rows of 128 bytes padded to 144 (row i of a 32-key sub-tile holds
+//     key perm_row(i)).  The padding puts the 16 rows that one pass of a
+//     ds_read_b128 touches on distinct banks.
+//  V: 128 rows of 128 bytes in natural key order, the two 64-byte halves of
+//     a row swapped when bit 1 of its index is set.  A transposed read
+//     (ds_read_b64_tr_b16) takes 64 bytes from each of four consecutive
+//     rows per pass; without the swap rows r and r+2 would share banks (with
+//     160-byte padded rows, 2 of the read's 4 LDS cycles were conflicts).
+// Every read address is a per-lane base plus an immediate.  Both tiles are
+// filled by global_load_lds_dwordx4 (global -> LDS without registers), 1 KB
+// (64 x 16 bytes) per instruction; granules that fall in K's padding load a
+// harmless in-range duplicate.
+constexpr int kKRow = 144, kVRow = 128;
+constexpr int kKTile = kBK * kKRow, kVTile = kBK * kVRow;     // 18432, 16384
+constexpr int kStage = kKTile + kVTile;                        // 34816
+constexpr int kKInstr = kKTile / 1024, kVInstr = kVTile / 1024;  // 18, 16
 constexpr int kDmaSlots = (kKInstr + kVInstr + 7) / 8;         // per wave: 5
 constexpr int kStages = 3;
 
@@ -241,7 +247,7 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
   if (tid == 0) fallback = 0;  // published by the first barrier below
 
   // ---- DMA plan: wave w issues the tile's 1 KB instructions w, w+8, ...
-  // (0..17: K, 18..37: V).  A lane's granule: key offset within the tile and
+  // (0..17: K, 18..33: V).  A lane's granule: key offset within the tile and
   // byte offset within the row.
   auto dma_granule = [&](int i, int& key, uint32_t& col) {
     if (i < kKInstr) {
@@ -249,9 +255,9 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
       key = (row & ~31) + perm_row(row & 31);
       col = gc < 8 ? gc * 16 : 0;
     } else {
-      const int g = (i - kKInstr) * 64 + lane, row = g / 10, gc = g % 10;
+      const int g = (i - kKInstr) * 64 + lane, row = g >> 3;
       key = row;
-      col = gc < 8 ? gc * 16 : 0;
+      col = (uint32_t)(((g & 7) ^ (row & 2 ? 4 : 0)) * 16);
     }
   };
   const char* kbytes = (const char*)p.k + (int64_t)head * 128;
@@ -298,10 +304,14 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
   };
 
   // per-lane LDS read bases: K operand (row l32 of a sub-tile, granule hf)
-  // and the V^T transposed read (16-lane group g reads 4 keys x 16 dims).
+  // and the V^T transposed read (16-lane group g reads 4 keys x 16 dims),
+  // one base per 32-dim half db.  The lane's rows all have bit 1 equal to
+  // bit 3 of j16, which decides whether its row halves are swapped.
   const int kread = l32 * kKRow + hf * 16;
   const int g16 = lane >> 4, j16 = lane & 15;
-  const int vread = kKTile + (8 * hf + (j16 >> 2)) * kVRow + (16 * (g16 & 1) + 4 * (j16 & 3)) * 2;
+  const int vlane = kKTile + (8 * hf + (j16 >> 2)) * kVRow + 32 * (g16 & 1) + 8 * (j16 & 3);
+  const int vswap = (j16 & 8) ? 64 : 0;
+  const int vread[2] = {vlane + vswap, vlane + 64 - vswap};
 
   // keys of the sub-tile at key0 that lie before the end of the range, as a
   // uniform count in [0, 32]: a key at offset j of the sub-tile is masked
@@ -353,12 +363,11 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
   };
   // O^T += V^T P^T; the V^T operand comes from two transposed reads
   auto pv = [&](int st, int sb, const u32x4 (&P)[2][2]) __attribute__((always_inline)) {
-    const char* sv = &lds[st][0] + vread + sb * 32 * kVRow;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
-        const char* a = sv + 16 * c2 * kVRow + db * 64;
+        const char* a = &lds[st][0] + vread[db] + sb * 32 * kVRow + 16 * c2 * kVRow;
         const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a);
         const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a + 4 * kVRow));
         const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -442,7 +451,7 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
   };
   // V^T operand (db, c2) of a sub-tile: two transposed reads
   auto load_v = [&](int st, int sb, int db, int c2) __attribute__((always_inline)) {
-    const char* a = &lds[st][0] + vread + sb * 32 * kVRow + 16 * c2 * kVRow + db * 64;
+    const char* a = &lds[st][0] + vread[db] + sb * 32 * kVRow + 16 * c2 * kVRow;
     const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a);
     const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a + 4 * kVRow));
     va[db][c2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
