@@ -680,28 +680,52 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
   if constexpr (KR == KeyRange::kSga) {
     // The diagonal and mean columns join each query's shared softmax here,
     // merged into (m, l, O) after the compacted keys (the softmax sums do not
-    // depend on the column order).
+    // depend on the column order).  Every load of the merge -- the query's
+    // own K and V rows and the mean columns -- is issued first, so the merge
+    // waits for memory once (the rows are in range: row < T; the mean
+    // columns always exist, zero when nothing is dropped).
     const uint16_t* kf = (const uint16_t*)p.k_full;
     const uint16_t* vf = (const uint16_t*)p.v_full;
+    const float* kms = p.kmean + head * 64 + 8 * hf;
+    const float* vms = p.vmean + head * 64;
+    u32x4 wk[2][4];
+    u32x2 wv[2][2][4];
+    f32x4 km[4][2], vm[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int64_t row = min(row0 + qb * 32, tr.q_end - 1);
+      const uint16_t* ks = kf + ((size_t)row * H + head) * 64 + 8 * hf;
+      const uint16_t* vs = vf + ((size_t)row * H + head) * 64;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) wk[qb][c] = *(const u32x4*)(ks + 16 * c);
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) wv[qb][db][g] = *(const u32x2*)(vs + 32 * db + 8 * g + 4 * hf);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      km[c][0] = *(const f32x4*)(kms + 16 * c);
+      km[c][1] = *(const f32x4*)(kms + 16 * c + 4);
+    }
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) vm[db][g] = *(const f32x4*)(vms + 32 * db + 8 * g + 4 * hf);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int64_t row = min(row0 + qb * 32, tr.q_end - 1);
       const bool diag = p.use_diag && !sga_kept(p.grid, p.row0 + row);
-      const uint16_t* ks = kf + ((size_t)row * H + head) * 64 + 8 * hf;
-      const float* kms = p.kmean + head * 64 + 8 * hf;
       float dk = 0.f, dm = 0.f;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const u32x4 wq = __builtin_bit_cast(u32x4, qreg[qb][c]);  // dims 16c + 8hf + [0, 8)
-        const u32x4 wk = *(const u32x4*)(ks + 16 * c);
-        const f32x4 m0 = *(const f32x4*)(kms + 16 * c);
-        const f32x4 m1 = *(const f32x4*)(kms + 16 * c + 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float qa = bf16_lo(wq[e]), qb2 = bf16_hi(wq[e]);
-          dk += qa * bf16_lo(wk[e]) + qb2 * bf16_hi(wk[e]);
-          const float ma = e < 2 ? m0[2 * e] : m1[2 * e - 4];
-          const float mb = e < 2 ? m0[2 * e + 1] : m1[2 * e - 3];
+          dk += qa * bf16_lo(wk[qb][c][e]) + qb2 * bf16_hi(wk[qb][c][e]);
+          const float ma = e < 2 ? km[c][0][2 * e] : km[c][1][2 * e - 4];
+          const float mb = e < 2 ? km[c][0][2 * e + 1] : km[c][1][2 * e - 3];
           dm += qa * ma + qb2 * mb;
         }
       }
@@ -717,19 +741,16 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
         const float wd = diag ? exp2f(zd - mn) : 0.f;
         const float wm = p.use_mean ? exp2f(zm - mn) : 0.f;
         lsum[qb] = lsum[qb] * f + (hf == 0 ? wd + wm : 0.f);
-        const uint16_t* vs = vf + ((size_t)row * H + head) * 64;
-        const float* vms = p.vmean + head * 64;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int d0 = 32 * db + 8 * g + 4 * hf;
-            const u32x2 wv = *(const u32x2*)(vs + d0);
-            const f32x4 mv = *(const f32x4*)(vms + d0);
-            o[qb][db][4 * g + 0] = o[qb][db][4 * g + 0] * f + wd * bf16_lo(wv[0]) + wm * mv[0];
-            o[qb][db][4 * g + 1] = o[qb][db][4 * g + 1] * f + wd * bf16_hi(wv[0]) + wm * mv[1];
-            o[qb][db][4 * g + 2] = o[qb][db][4 * g + 2] * f + wd * bf16_lo(wv[1]) + wm * mv[2];
-            o[qb][db][4 * g + 3] = o[qb][db][4 * g + 3] * f + wd * bf16_hi(wv[1]) + wm * mv[3];
+            const u32x2 w = wv[qb][db][g];
+            const f32x4 mv = vm[db][g];
+            o[qb][db][4 * g + 0] = o[qb][db][4 * g + 0] * f + wd * bf16_lo(w[0]) + wm * mv[0];
+            o[qb][db][4 * g + 1] = o[qb][db][4 * g + 1] * f + wd * bf16_hi(w[0]) + wm * mv[1];
+            o[qb][db][4 * g + 2] = o[qb][db][4 * g + 2] * f + wd * bf16_lo(w[1]) + wm * mv[2];
+            o[qb][db][4 * g + 3] = o[qb][db][4 * g + 3] * f + wd * bf16_hi(w[1]) + wm * mv[3];
           }
       }
     }
