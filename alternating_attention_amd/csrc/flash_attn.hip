@@ -213,13 +213,43 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
   const float qscale = p.scale * kLog2e;
   const int64_t row_bytes = (int64_t)H * 128;
 
+  // ---- this wave's query blocks (32 rows each, at most two).  In a full
+  // workgroup wave w has rows 64w .. 64w+63.  In frame attention a ragged
+  // workgroup (nb < 16 blocks: a 1,374-token frame's last 350 rows are 11)
+  // spreads its blocks over the four SIMDs as evenly as possible: SIMD s
+  // (waves s and s+4) takes nb/4 blocks, or one more for s < nb%4, wave s
+  // up to two of them, and blocks are numbered in wave order.  A workgroup
+  // lasts as long as its busiest SIMD's products, and the key loop skips
+  // the products of absent blocks (a wave with one block runs the
+  // one-block step, a wave with none only its share of the tile DMA and the
+  // barriers).  Global and SGA attention, whose only ragged workgroup is a
+  // head's last, keep two blocks per wave.
+  int64_t wq_begin = tr.q_begin + wave * kQPerWave;   // this wave's rows
+  int64_t wq_end = tr.q_end;                           // (stores stop here)
+  int nblk = 2;
+  if constexpr (KR == KeyRange::kFrame) {
+    const int nb = (int)((tr.q_end - tr.q_begin + 31) >> 5);  // 1 .. 16
+    int first_blk = 0;
+    for (int w = 0; w <= wave; ++w) {
+      const int cs = (nb >> 2) + ((w & 3) < (nb & 3) ? 1 : 0);
+      const int n0 = cs < 2 ? cs : 2;
+      const int nw = w < 4 ? n0 : cs - n0;
+      if (w < wave)
+        first_blk += nw;
+      else
+        nblk = nw;
+    }
+    wq_begin = tr.q_begin + 32 * first_blk;
+    wq_end = min(wq_begin + 32 * nblk, tr.q_end);
+  }
+
   // ---- Q block of this wave into registers (B operand of S^T = K Q^T):
-  // lane holds query l32 of block qb (clamped into range), dims
-  // 16c + 8*hf + [0, 8), as stored.
+  // lane holds query l32 of block qb (clamped into the workgroup's rows),
+  // dims 16c + 8*hf + [0, 8), as stored.
   bf16x8 qreg[2][4];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int64_t row = min(tr.q_begin + wave * kQPerWave + qb * 32 + l32, tr.q_end - 1);
+    const int64_t row = min(wq_begin + qb * 32 + l32, tr.q_end - 1);
     const uint16_t* src = qg + ((size_t)row * H + head) * 64 + 8 * hf;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -474,9 +504,10 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
   // PV(j-1), and block 1's reference max is taken at unit 8, once its
   // scores exist.  Tail: keys at or past the end of the range get P = 0.
   auto step = [&](int stK, int sbK, int stV, int sbV, int64_t key0, auto first_tag,
-                  auto tail_tag) __attribute__((always_inline)) {
+                  auto tail_tag, auto nb_tag) __attribute__((always_inline)) {
     constexpr bool first = decltype(first_tag)::value;
     constexpr bool tail = decltype(tail_tag)::value;
+    constexpr bool two = decltype(nb_tag)::value == 2;  // else block 0 only
     const int lim = tail ? valid(key0) : 32;
     // softmax of pair w (operand half w/4, register pair w%4) of block qb:
     // z = scale*S - m (log2 units), P = exp2(z) as bf16
@@ -506,16 +537,17 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
       // V operands in the order the PV units use them: (db, c2) = (0,0),
       // (1,0), (0,1), (1,1), so consecutive PV MFMAs alternate accumulators
       if (u >= 8 && u < 12) load_v(stV, sbV, (u - 8) & 1, (u - 8) >> 1);
-      if (first && u == 8) {
+      if (two && first && u == 8) {
         m[1] = subtile_max(S[1], key0, tail_tag) * qscale;
         mset[1] = true;
       }
-      pair(u >> 3, u & 7);
+      if (two || u < 8) pair(u >> 3, u & 7);
       if (u < 4) {
-        S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[u], qreg[1][u],
-                                                       u == 0 ? f32x16(0.f) : S[1], 0, 0, 0);
+        if constexpr (two)
+          S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[u], qreg[1][u],
+                                                         u == 0 ? f32x16(0.f) : S[1], 0, 0, 0);
       } else if (u < 8) {
-        if constexpr (!first) {
+        if constexpr (two && !first) {
           const int db = (u - 4) & 1, c2 = (u - 4) >> 1;
           o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               va[db][c2], __builtin_bit_cast(bf16x8, P[1][c2]), o[1][db], 0, 0, 0);
@@ -565,59 +597,91 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
     __syncthreads();
     if (t + 2 < ntiles) issue_tile(t + 2, st_prev);
   };
-  // ---- tile 0 (the ragged tail when there is one): steps 0..3.  Before
-  // step 0: K operands and block 0's scores of sub-tile 0, and block 0's
-  // reference max (sub-tile 0 holds at least one key).
-  const int64_t key00 = tile_key0(0);
-  const int st1 = ntiles > 1 ? 1 : 0;  // K source of step 3 (a dummy re-read if no tile 1)
-#pragma unroll
-  for (int c = 0; c < 4; ++c) load_k(0, 0, c);
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-    S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qreg[0][c], c == 0 ? f32x16(0.f) : S[0],
-                                                   0, 0, 0);
   constexpr std::true_type yes{};
   constexpr std::false_type no{};
-  if (has_tail) {
-    m[0] = subtile_max(S[0], key00, yes) * qscale;
-    mset[0] = true;
-    step(0, 1, 0, 0, key00, yes, yes);
-    step(0, 2, 0, 1, key00 + 32, no, yes);
-    step(0, 3, 0, 2, key00 + 64, no, yes);
-    if (ntiles > 1) advance(0, kStages - 1);
-    step(st1, 0, 0, 3, key00 + 96, no, yes);
+  constexpr std::integral_constant<int, 2> kTwo{};
+  constexpr std::integral_constant<int, 1> kOne{};
+  // The key loop of a wave with NB query blocks (NB_TAG: kTwo or kOne), expanded in place for each
+  // block count so that every expansion compiles as the kernel's own
+  // straight-line code (wrapped in a lambda, the compiler schedules the
+  // global and SGA loops differently, and measurably slower).
+#define VGA_KEY_LOOP(NB_TAG)                                                                       \
+  do {                                                                                             \
+    /* ---- tile 0 (the ragged tail when there is one): steps 0..3.  Before */                     \
+    /* step 0: K operands and block 0's scores of sub-tile 0, and block 0's */                     \
+    /* reference max (sub-tile 0 holds at least one key). */                                       \
+    const int64_t key00 = tile_key0(0);                                                            \
+    const int st1 = ntiles > 1 ? 1 : 0;  /* K source of step 3 (a dummy re-read if no tile 1) */   \
+  _Pragma("unroll")                                                                                \
+    for (int c = 0; c < 4; ++c) load_k(0, 0, c);                                                   \
+  _Pragma("unroll")                                                                                \
+    for (int c = 0; c < 4; ++c)                                                                    \
+      S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qreg[0][c], c == 0 ? f32x16(0.f) : S[0], \
+                                                     0, 0, 0);                                     \
+    if (has_tail) {                                                                                \
+      m[0] = subtile_max(S[0], key00, yes) * qscale;                                               \
+      mset[0] = true;                                                                              \
+      step(0, 1, 0, 0, key00, yes, yes, NB_TAG);                                                   \
+      step(0, 2, 0, 1, key00 + 32, no, yes, NB_TAG);                                               \
+      step(0, 3, 0, 2, key00 + 64, no, yes, NB_TAG);                                               \
+      if (ntiles > 1) advance(0, kStages - 1);                                                     \
+      step(st1, 0, 0, 3, key00 + 96, no, yes, NB_TAG);                                             \
+    } else {                                                                                       \
+      m[0] = subtile_max(S[0], key00, no) * qscale;                                                \
+      mset[0] = true;                                                                              \
+      step(0, 1, 0, 0, 0, yes, no, NB_TAG);                                                        \
+      step(0, 2, 0, 1, 0, no, no, NB_TAG);                                                         \
+      step(0, 3, 0, 2, 0, no, no, NB_TAG);                                                         \
+      if (ntiles > 1) advance(0, kStages - 1);                                                     \
+      step(st1, 0, 0, 3, 0, no, no, NB_TAG);                                                       \
+    }                                                                                              \
+    /* ---- full tiles 1 .. ntiles-1: steps 4t .. 4t+3 */                                          \
+    int st = 0;                                                                                    \
+    for (int32_t t = 1; t < ntiles; ++t) {                                                         \
+      const int st_prev = st;                                                                      \
+      st = st == kStages - 1 ? 0 : st + 1;                                                         \
+      const int st_next = st == kStages - 1 ? 0 : st + 1;                                          \
+      const bool has_next = t + 1 < ntiles;                                                        \
+      step(st, 1, st, 0, 0, no, no, NB_TAG);                                                       \
+      step(st, 2, st, 1, 0, no, no, NB_TAG);                                                       \
+      step(st, 3, st, 2, 0, no, no, NB_TAG);                                                       \
+      if (has_next) advance(t, st_prev);                                                           \
+      /* K of sub-tile 4t+4 (tile t+1); a dummy re-read of this tile when t is last */             \
+      step(has_next ? st_next : st, 0, st, 3, 0, no, no, NB_TAG);                                  \
+    }                                                                                              \
+    /* drain: PV and row sums of the last sub-tile's block 1 */                                    \
+    if constexpr (decltype(NB_TAG)::value == 2) {                                                  \
+  _Pragma("unroll")                                                                                \
+      for (int c2 = 0; c2 < 2; ++c2) {                                                             \
+  _Pragma("unroll")                                                                                \
+        for (int db = 0; db < 2; ++db)                                                             \
+          o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                                      \
+              va[db][c2], __builtin_bit_cast(bf16x8, P[1][c2]), o[1][db], 0, 0, 0);                \
+        rowsum(1, P[1][c2]);                                                                       \
+      }                                                                                            \
+    }                                                                                              \
+  } while (0)
+  if constexpr (KR == KeyRange::kFrame) {
+    // A wave without query blocks takes part in the tile DMA and the
+    // barriers exactly as the key loop does: advance() after tile 0's third
+    // step and after each later tile's third step but the last's.
+    if (nblk == 2) {
+      VGA_KEY_LOOP(kTwo);
+    } else if (nblk == 1) {
+      VGA_KEY_LOOP(kOne);
+    } else {
+      if (ntiles > 1) advance(0, kStages - 1);
+      int st = 0;
+      for (int32_t t = 1; t < ntiles; ++t) {
+        const int st_prev = st;
+        st = st == kStages - 1 ? 0 : st + 1;
+        if (t + 1 < ntiles) advance(t, st_prev);
+      }
+    }
   } else {
-    m[0] = subtile_max(S[0], key00, no) * qscale;
-    mset[0] = true;
-    step(0, 1, 0, 0, 0, yes, no);
-    step(0, 2, 0, 1, 0, no, no);
-    step(0, 3, 0, 2, 0, no, no);
-    if (ntiles > 1) advance(0, kStages - 1);
-    step(st1, 0, 0, 3, 0, no, no);
+    VGA_KEY_LOOP(kTwo);
   }
-  // ---- full tiles 1 .. ntiles-1: steps 4t .. 4t+3
-  int st = 0;
-  for (int32_t t = 1; t < ntiles; ++t) {
-    const int st_prev = st;
-    st = st == kStages - 1 ? 0 : st + 1;
-    const int st_next = st == kStages - 1 ? 0 : st + 1;
-    const bool has_next = t + 1 < ntiles;
-    step(st, 1, st, 0, 0, no, no);
-    step(st, 2, st, 1, 0, no, no);
-    step(st, 3, st, 2, 0, no, no);
-    if (has_next) advance(t, st_prev);
-    // K of sub-tile 4t+4 (tile t+1); a dummy re-read of this tile when t is last
-    step(has_next ? st_next : st, 0, st, 3, 0, no, no);
-  }
-  // drain: PV and row sums of the last sub-tile's block 1
-#pragma unroll
-  for (int c2 = 0; c2 < 2; ++c2) {
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-      o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          va[db][c2], __builtin_bit_cast(bf16x8, P[1][c2]), o[1][db], 0, 0, 0);
-    rowsum(1, P[1][c2]);
-  }
+#undef VGA_KEY_LOOP
 
   // Row sums into the lane of their query (lane L holds query L % 32):
   // accumulator lane L % 32 (< 16) or L % 32 + 16 (>= 16) has it.
@@ -674,7 +738,7 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
 
   // This wave's first query row, recomputed here: the value from the Q load
   // would otherwise be kept, in registers or scratch, across the loop.
-  int64_t row0 = tr.q_begin + wave * kQPerWave + l32;
+  int64_t row0 = wq_begin + l32;
   asm volatile("" : "+v"(row0));
 
   if constexpr (KR == KeyRange::kSga) {
@@ -763,7 +827,7 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
     const float l = lsum[qb] + __shfl_xor(lsum[qb], 32);
     const float inv = 1.f / l;
     const int64_t row = row0 + qb * 32;
-    if (row < tr.q_end) {
+    if (row < wq_end) {
       uint16_t* dst = og + ((size_t)row * H + head) * 64;
 #pragma unroll
       for (int db = 0; db < 2; ++db)

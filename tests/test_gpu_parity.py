@@ -172,6 +172,20 @@ def test_small_shapes(vga, shape, dt):
                     tag="%s-%s" % (shape, dt))
 
 
+@pytest.mark.parametrize("nb_last", range(1, 17))
+def test_ragged_workgroup_blocks(vga, nb_last):
+    # One frame of L = 507 + 32 * nb_last tokens: the second 512-query
+    # workgroup holds nb_last 32-row blocks, the last of them 27 rows.  The
+    # bf16 kernel spreads them over its waves (one, two or no blocks each)
+    # and skips absent blocks; every output row is compared.
+    L = 507 + 32 * nb_last
+    frames = vga.Frames(1, 2, (L - 1) // 2, 1, 2)
+    assert frames.tokens == L
+    q, k, v = to_dev(tiny_qkv(L, 2, 64, seed=300 + nb_last), torch.bfloat16)
+    run_and_compare(vga, frames, q, k, v, ["frame", "global"],
+                    [vga.Sga(2, 2, 0, 0, True, True)], tag="nb_last=%d" % nb_last)
+
+
 @pytest.mark.parametrize("dt,H", [("bf16", 64), ("f32", 32)])
 def test_most_heads(vga, dt, H):
     # the largest head counts the ABI accepts (64 in bf16, 32 in fp32): the
