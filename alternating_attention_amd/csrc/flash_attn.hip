@@ -13,7 +13,9 @@
 //              one softmax.
 //
 // bf16 path (MFMA).  A workgroup of 8 waves (two per SIMD) owns 512 queries
-// of one head; each wave owns 64 queries as two 32-query blocks.  Scores are
+// of one head; each wave owns 64 queries as two 32-query blocks (a ragged
+// frame workgroup spreads its blocks over the SIMDs instead, and waves skip
+// the products of blocks they lack).  Scores are
 // computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: keys
 // index the accumulator rows and queries its columns, so every lane holds
 // 16 scores of ONE query.  Row statistics therefore stay in the lane (plus
@@ -24,7 +26,7 @@
 // B-operand k-slot order of the PV product.  V stays in its natural layout;
 // the PV A operand (V^T) comes from ds_read_b64_tr_b16 transposed reads.
 // K/V tiles of 128 keys move global -> LDS with global_load_lds_dwordx4 (no
-// registers) through a ring of three stages (114 KB: one workgroup per CU);
+// registers) through a ring of three stages (102 KB: one workgroup per CU);
 // a ragged last tile is taken first (softmax sums do not depend on the key
 // order), so every later tile is full and needs no masking; the ragged tile
 // runs the same pipelined steps with its keys past the end masked.
