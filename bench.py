@@ -295,6 +295,9 @@ def run(args):
     torch.cuda.synchronize()
     out = torch.empty_like(q)
     out_b = torch.empty_like(q)
+    # the layer that precedes the SGA layer in the step, if any (the SGA
+    # selection row is timed behind it)
+    sel_prev = None
     timers = {}
     step_counts = None   # per kind of layer (modes, then SGA list) when the step repeats them
 
@@ -338,6 +341,7 @@ def run(args):
             timed("frame", lambda: vga.frame_attn(q, k, v, frames, out))
             timed("global", lambda: vga.global_attn(q, k, v, frames, out))
             timed("sga", lambda: vga.sga_attn(q, k, v, frames, sga, out_b, ws))
+        sel_prev = ("the exact global layer", lambda: vga.global_attn(q, k, v, frames, out))
         work = {"frame": flops_frame(N, L, H), "global": flops_global(T, H),
                 "sga": flops_sga(T, nk, H)}
         dominant, modes, sgas = "global", ["frame", "global"], [sga]
@@ -352,6 +356,7 @@ def run(args):
         def step():
             timed("global", lambda: vga.global_attn(q, k, v, frames, out))
             timed("sga", lambda: vga.sga_attn(q, k, v, frames, sga, out_b, ws))
+        sel_prev = ("the exact global layer", lambda: vga.global_attn(q, k, v, frames, out))
         work = {"global": flops_global(T, H), "sga": flops_sga(T, nk, H)}
         dominant, modes, sgas = "global", ["global"], [sga]
     elif args.workload == "n800":
@@ -434,6 +439,8 @@ def run(args):
         def step():
             timed("global", lambda: vga.global_attn_rows(qr, k, v, frames, r0, o_r))
             timed("sga", lambda: vga.sga_attn_rows(qr, k, v, frames, sga, r0, o_r, ws))
+        sel_prev = ("the row-range global layer",
+                    lambda: vga.global_attn_rows(qr, k, v, frames, r0, o_r))
         work = {"global": 4.0 * (r1 - r0) * T * HEAD_DIM * H,
                 "sga": 4.0 * (r1 - r0) * nk * HEAD_DIM * H}
         dominant, modes, sgas = "global", ["global"], [sga]
@@ -510,9 +517,8 @@ def run(args):
         # calls queued back to back (each behind the previous call's writes)
         # and one call on an idle stream (which also counts the launch
         # latency).
-        if "global" in per:
-            prev_name = "the exact global layer"
-            prev = lambda: vga.global_attn(q, k, v, frames, out)
+        if sel_prev is not None:
+            prev_name, prev = sel_prev
         else:
             prev_name = "an SGA layer"
             prev = lambda: vga.sga_attn(q, k, v, frames, sga, out_b, ws)
