@@ -824,6 +824,43 @@ __global__ void __launch_bounds__(kThreads, 1) flash_bf16_kernel(FlashParams p) 
 
   // ---- normalise and store O (bf16, RNE)
   uint16_t* __restrict__ og = (uint16_t*)p.o;
+  if constexpr (KR == KeyRange::kFrame) {
+    // Frame attention (short workgroups, where the epilogue weighs): the
+    // wave stages its 64 rows in LDS and writes whole 128-byte rows with
+    // 16-byte stores, 8 lanes per row.  Each wave has its own 8 KB in the
+    // ring's stages 1-2, which no wave reads after the key loop (the exact
+    // fallback uses stage 0 only); 16-byte slot g of staged row r sits at
+    // slot g ^ ((r >> 1) & 7).  LDS operations of one wave complete in
+    // order, so the reads see the writes without a barrier.
+    char* stg = &lds[1][0] + wave * 8192;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float l = lsum[qb] + __shfl_xor(lsum[qb], 32);
+      const float inv = 1.f / l;
+      const int r = qb * 32 + l32;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2 w;
+          w[0] = pack_bf16(o[qb][db][4 * g + 0] * inv, o[qb][db][4 * g + 1] * inv);
+          w[1] = pack_bf16(o[qb][db][4 * g + 2] * inv, o[qb][db][4 * g + 3] * inv);
+          const int slot = (4 * db + g) ^ ((r >> 1) & 7);
+          *(__attribute__((address_space(3))) u32x2*)(stg + r * 128 + slot * 16 + 8 * hf) = w;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int r = 8 * k + (lane >> 3), g = lane & 7;
+      const u32x4 w = *(const lds_u32x4*)(stg + r * 128 + ((g ^ ((r >> 1) & 7)) * 16));
+      const int64_t row = wq_begin + r;
+      if (row < wq_end) *(u32x4*)(og + ((size_t)row * H + head) * 64 + 8 * g) = w;
+    }
+    return;
+  }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float l = lsum[qb] + __shfl_xor(lsum[qb], 32);
